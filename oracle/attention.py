@@ -1,0 +1,150 @@
+"""Plain fp64 softmax attention: the result the ring reaches (test infrastructure).
+
+The ring of the pages ends with every device holding "the correct output for its
+local Q tokens", and the Ultralytics glossary ("How Context Parallelism Works")
+states that the result equals full-sequence attention up to ordinary rounding.
+Neither page writes the formula out; the Ultralytics example ("Practical Use and
+Tradeoffs") names it as PyTorch's scaled dot-product attention with
+``is_causal=True``. So this module is that textbook definition, computed
+directly over the whole global key set. It never sees blocks, ring steps, chunk
+assignments or running state.
+
+For a query row i at global position g(i), with visible key set V(i):
+    s_ij  = scale * <q_i, k_j>
+    M_i   = max_{j in V(i)} s_ij
+    o_i   = sum_j exp(s_ij - M_i) v_j / sum_j exp(s_ij - M_i)
+    lse_i = M_i + ln sum_j exp(s_ij - M_i)
+V(i) is every key for the unmasked case and {j : g(j) <= g(i)} for the causal
+case (the diagonal is visible). A row with no visible key has o_i = 0 and
+lse_i = -inf.
+
+Only tests/, the smoke check and the CPU-baseline leg of the benchmark use this.
+"""
+
+import numpy as np
+
+_NEG_INF = -np.inf
+
+
+def attention_rows(q, q_pos, k, v, k_pos, scale, causal, row_chunk=256):
+    """Softmax attention of query rows against a global key/value set.
+
+    Definition: Day 83 post, "Context parallelism: splitting the sequence"
+    (the ring's end state is full attention for the local queries); Ultralytics
+    glossary, "How Context Parallelism Works" (equivalence with full-sequence
+    attention) and "Practical Use and Tradeoffs" (scaled dot-product attention,
+    causal).
+
+    q      (n, d)  query rows; upcast to fp64 from the exact values given
+    q_pos  (n,)    global token position of each query row
+    k, v   (S, d)  keys and values of the global sequence
+    k_pos  (S,)    global position of each key row
+    scale  float   multiplier on the dot products
+    causal bool    if True, key j is visible to query i iff k_pos[j] <= q_pos[i]
+    returns (o (n, d) fp64, lse (n,) fp64, natural log)
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    n, d = q.shape
+    o = np.zeros((n, v.shape[1]), dtype=np.float64)
+    lse = np.full((n,), _NEG_INF, dtype=np.float64)
+    for r0 in range(0, n, row_chunk):
+        r1 = min(n, r0 + row_chunk)
+        s = float(scale) * (q[r0:r1] @ k.T)
+        if causal:
+            visible = k_pos[None, :] <= q_pos[r0:r1, None]
+            s = np.where(visible, s, _NEG_INF)
+        row_max = s.max(axis=1)
+        has_key = np.isfinite(row_max)
+        shift = np.where(has_key, row_max, 0.0)
+        w = np.exp(s - shift[:, None])  # exp(-inf) = 0 for masked keys
+        denom = w.sum(axis=1)
+        num = w @ v
+        safe = np.where(has_key, denom, 1.0)
+        o[r0:r1] = np.where(has_key[:, None], num / safe[:, None], 0.0)
+        lse[r0:r1] = np.where(has_key, shift + np.log(safe), _NEG_INF)
+    return o, lse
+
+
+def factored_spatial(q, k, v, T, S_sp, scale):
+    """Spatial attention of a frame-major video token sequence.
+
+    Day 83 post, "The spatial-temporal twist": factored video attention runs
+    spatial attention inside each frame. Token index = t * S_sp + s. Each query
+    at (t, s) attends, without a mask, to the S_sp keys of its own frame t.
+
+    q, k, v (T*S_sp, d); returns (o (T*S_sp, d), lse (T*S_sp,)).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    o = np.zeros_like(v, dtype=np.float64)
+    lse = np.zeros((T * S_sp,), dtype=np.float64)
+    pos = np.arange(S_sp)
+    for t in range(T):
+        rows = slice(t * S_sp, (t + 1) * S_sp)
+        o[rows], lse[rows] = attention_rows(q[rows], pos, k[rows], v[rows], pos,
+                                            scale, causal=False)
+    return o, lse
+
+
+def factored_temporal(q, k, v, T, S_sp, scale):
+    """Temporal attention of a frame-major video token sequence.
+
+    Day 83 post, "The spatial-temporal twist": temporal attention runs across
+    frames. A query at (t, s) attends, without a mask, to the T keys
+    {t' * S_sp + s : t' < T} at the same spatial position s.
+
+    q, k, v (T*S_sp, d); returns (o (T*S_sp, d), lse (T*S_sp,)).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d = q.shape[1]
+    # (T, S_sp, d) -> (S_sp, T, d): one length-T problem per spatial position.
+    qs = q.reshape(T, S_sp, d).transpose(1, 0, 2)
+    ks = k.reshape(T, S_sp, d).transpose(1, 0, 2)
+    vs = v.reshape(T, S_sp, d).transpose(1, 0, 2)
+    s = float(scale) * np.matmul(qs, ks.transpose(0, 2, 1))  # (S_sp, T, T)
+    row_max = s.max(axis=2, keepdims=True)
+    w = np.exp(s - row_max)
+    denom = w.sum(axis=2, keepdims=True)
+    o = np.matmul(w, vs) / denom  # (S_sp, T, d)
+    lse = (row_max + np.log(denom))[..., 0]  # (S_sp, T)
+    return (o.transpose(1, 0, 2).reshape(T * S_sp, d),
+            lse.transpose(1, 0).reshape(T * S_sp))
+
+
+def merge_lse(o_a, lse_a, o_b, lse_b):
+    """Combine two normalised partial attentions over disjoint key sets.
+
+    Day 83 post, "Context parallelism: splitting the sequence": each device
+    accumulates partial attention outputs with the online-softmax rule. For
+    partial results over disjoint key sets A and B, the softmax weights of the
+    union are the partial weights rescaled by exp(lse_part - lse_union):
+        lse = ln(exp(lse_a) + exp(lse_b))
+        o   = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b
+    A side with lse = -inf (no keys) has weight 0; if both sides are empty the
+    result is o = 0, lse = -inf.
+
+    o_* (n, d), lse_* (n,); returns (o (n, d), lse (n,)) in fp64.
+    """
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    hi = np.maximum(lse_a, lse_b)
+    empty = ~np.isfinite(hi)
+    ref = np.where(empty, 0.0, hi)
+    ea = np.exp(lse_a - ref)  # exp(-inf) = 0 for an empty side
+    eb = np.exp(lse_b - ref)
+    tot = ea + eb
+    safe = np.where(empty, 1.0, tot)
+    lse = np.where(empty, _NEG_INF, ref + np.log(safe))
+    wa = np.where(empty, 0.0, ea / safe)
+    wb = np.where(empty, 0.0, eb / safe)
+    o = wa[:, None] * o_a + wb[:, None] * o_b
+    return o, lse
