@@ -1,0 +1,292 @@
+"""Benchmark: attention TFLOP/s of one rank's ring-attention share on one MI355X.
+
+One "step" is one full pass of the hot path over the workload: the P ring steps
+(``ra_step`` on the compute stream, the next K/V block passed on a side stream
+with ``ra_kv_pass``) and ``ra_finalize``. Inputs are seeded synthetic tensors
+already resident in HBM before the timed region. The default workload is the
+32K-token causal LLM context, share of rank 0 of 4 (zigzag split).
+
+Printed: one JSON line. ``value`` is whole-pass throughput (algorithmic FLOP =
+4*d per unmasked query/key pair) over the wall time of the timed steps.
+``roofline`` is the ring-step kernel's algorithmic FLOP per launch over its
+mean launch time (HIP events on the compute stream) against the bf16 dense
+matrix-core peak. ``legs`` times the remaining kernels of the path on their
+own workloads (merge on this workload's shapes; factored spatial/temporal on
+the 16x900 video workload). ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import seeded  # noqa: E402
+from context_attention_ra_amd import _lib, configs, layout, ring, sizing  # noqa: E402
+
+PEAK_BF16_DENSE = 2.5e15    # MI355X bf16 dense matrix-core FLOP/s (published)
+PEAK_HBM = 8.0e12           # MI355X HBM3E bytes/s (published)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def positions(segs):
+    return np.concatenate([np.arange(s, s + n, dtype=np.int64) for s, n in segs])
+
+
+def make_ring_inputs(w, rank, dev):
+    segs = [layout.split(w.split, w.S, w.P, t, S_sp=w.S_sp) for t in range(w.P)]
+    pos = [torch.as_tensor(positions(s), device=dev) for s in segs]
+    q = seeded.gen_bhsd_at(w.wid, seeded.Q, w.B, w.H, positions(segs[rank]), w.d, w.dtype, dev)
+    kv = [(torch.empty((w.B, w.H, w.L, w.d), dtype=w.dtype, device=dev),
+           torch.empty((w.B, w.H, w.L, w.d), dtype=w.dtype, device=dev)) for _ in range(w.P)]
+    for b in range(w.B):
+        for h in range(w.H):
+            for tid, slot in ((seeded.K, 0), (seeded.V, 1)):
+                g = seeded.to_dtype(seeded.normal_rows(w.wid, tid, b, h, 0, w.S, w.d), w.dtype).to(dev)
+                for t in range(w.P):
+                    kv[t][slot][b, h] = g.index_select(0, pos[t])
+    return q, segs, kv
+
+
+def ring_flop(w, rank, segs):
+    order = layout.ring_order(rank, w.P)
+    per_step = [sizing.pairs(segs[rank], segs[t], w.causal) for t in order]
+    return [sizing.attention_flop(p, w.d, w.B * w.H) for p in per_step]
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "context_attention_ra_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from committed counter summaries, if still current."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_ring(w, rank, q, segs, kv, steps, warmup, prefetch):
+    dev = q.device
+    st = ring.RingState(w.B, w.H, w.L, w.d, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+    bufs = [(torch.empty_like(kv[0][0]), torch.empty_like(kv[0][1])) for _ in range(2)]
+    side = torch.cuda.Stream(dev)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.P)] for _ in range(steps)]
+
+    def one(events=None):
+        ring.run(q, segs[rank], kv, segs, rank, w.causal, scale=w.scale, prefetch=prefetch,
+                 out=out, lse=lse, state=st, bufs=bufs, copy_stream=side, step_events=events)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([[a.elapsed_time(b) for a, b in e] for e in ev])  # [steps, P] ms
+    return wall, kms, out, lse
+
+
+def time_kernel(fn, reps, warmup=3):
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        e0[i].record()
+        fn()
+        e1[i].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)]))
+
+
+def legs(w, q, dev, reps):
+    out = {}
+    # LSE merge of two normalised partials of this workload's shape (bf16)
+    B, H, L, d = q.shape
+    oa = torch.randn_like(q)
+    ob = torch.randn_like(q)
+    la = torch.randn((B, H, L), device=dev)
+    lb = torch.randn((B, H, L), device=dev)
+    oo, lo = torch.empty_like(q), torch.empty_like(la)
+    ms = time_kernel(lambda: _lib.ra_merge_lse(oa, la, ob, lb, oo, lo), reps)
+    nbytes = 3 * q.numel() * q.element_size() + 3 * la.numel() * 4
+    out["merge_lse"] = {"workload": f"{w.name} rank share [B,H,L,d]={list(q.shape)} bf16",
+                        "ms": ms, "GB/s": nbytes / ms / 1e6, "hbm_frac": nbytes / ms / 1e-3 / PEAK_HBM}
+    # factored video attention, 16 frames x 900 tokens
+    v = configs.VIDEO_FACTORED
+    qv, kvv, vv = (seeded.gen_bhsd(v.wid, tid, v.B, v.H, 0, v.N, v.d, v.dtype, dev)
+                   for tid in (seeded.Q, seeded.K, seeded.V))
+    ov = torch.empty_like(qv)
+    lv = torch.empty((v.B, v.H, v.N), dtype=torch.float32, device=dev)
+    ms = time_kernel(lambda: _lib.ra_factored_spatial(qv, kvv, vv, v.T, v.S_sp, v.scale, ov, lv), reps)
+    fl = sizing.attention_flop(v.T * v.S_sp * v.S_sp, v.d, v.B * v.H)
+    out["factored_spatial"] = {"workload": v.name, "ms": ms, "TFLOP/s": fl / ms / 1e9,
+                               "mfma_frac": fl / ms / 1e-3 / PEAK_BF16_DENSE}
+    # temporal: flush caches between reps by touching a 1 GiB buffer
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def temporal():
+        _lib.ra_factored_temporal(qv, kvv, vv, v.T, v.S_sp, v.scale, ov, lv)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tms = []
+    for i in range(reps + 2):
+        flush.fill_(float(i))
+        e0.record()
+        temporal()
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            tms.append(e0.elapsed_time(e1))
+    ms = float(np.mean(tms))
+    nbytes = 4 * qv.numel() * qv.element_size() + lv.numel() * 4
+    out["factored_temporal"] = {"workload": v.name, "ms": ms, "GB/s": nbytes / ms / 1e6,
+                                "hbm_frac": nbytes / ms / 1e-3 / PEAK_HBM,
+                                "algorithmic_bytes": nbytes, "caches": "flushed (1 GiB write) before each rep"}
+    return out
+
+
+def cpu_baseline(w, rank, segs, budget_s):
+    """The oracle, as it stands, on a bounded sample of this workload's rows."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    qpos_all = positions(segs[rank])
+    chunk = 256
+    rng = np.random.default_rng(7)
+    done_rows, flop, elapsed = 0, 0.0, 0.0
+    heads = []
+    h = 0
+    while elapsed < budget_s and h < w.B * w.H:
+        b, hh = divmod(h, w.H)
+        kf = seeded.exact_f64(seeded.to_dtype(seeded.normal_rows(w.wid, seeded.K, b, hh, 0, w.S, w.d), w.dtype))
+        vf = seeded.exact_f64(seeded.to_dtype(seeded.normal_rows(w.wid, seeded.V, b, hh, 0, w.S, w.d), w.dtype))
+        r0 = int(rng.integers(0, max(1, qpos_all.size - chunk)))
+        qp = qpos_all[r0:r0 + chunk]
+        qf = seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, seeded.Q, b, hh, qp, w.d), w.dtype))
+        t0 = time.perf_counter()
+        oracle.attention_rows(qf, qp, kf, vf, np.arange(w.S), w.scale, w.causal)
+        elapsed += time.perf_counter() - t0
+        pairs = int(np.minimum(qp + 1, w.S).sum()) if w.causal else qp.size * w.S
+        flop += sizing.attention_flop(pairs, w.d, 1)
+        done_rows += qp.size
+        heads.append(h)
+        h += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_rows} query rows ({chunk}-row runs from {len(heads)} heads) of rank {rank} "
+                      f"against the full {w.S}-token K/V, fp64 numpy; {elapsed:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=configs.LLM_32K_CP4.name, choices=sorted(configs.RING_WORKLOADS))
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--no-prefetch", action="store_true", help="pass each block on the compute stream")
+    ap.add_argument("--no-legs", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain 'copy_' of this many MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    _lib.load()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 18
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}))
+        return
+
+    w = configs.RING_WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name} rank {args.rank}: generating inputs")
+    q, segs, kv = make_ring_inputs(w, args.rank, dev)
+    flops = ring_flop(w, args.rank, segs)
+    total = float(sum(flops))
+    log(f"[bench] {w.P} ring steps, {total:.4e} algorithmic FLOP per pass; timing {args.steps} passes")
+    wall, kms, out, lse = time_ring(w, args.rank, q, segs, kv, args.steps, args.warmup, not args.no_prefetch)
+    assert torch.isfinite(lse).all(), "non-finite lse"
+    ms_per_step = wall / args.steps * 1e3
+    value = total * args.steps / wall / 1e12
+    k_mean_ms = float(kms.mean())
+    achieved = (total / w.P) / (k_mean_ms * 1e-3)
+    src_hash = kernel_source_hash(["step_mfma.hip"] if w.dtype == torch.bfloat16 else ["step_f32.hip"])
+    traffic = load_traffic("ra_step:" + w.name, src_hash)
+    rec = {
+        "metric": "attention TFLOP/s per MI355X (and % bf16 MFMA peak), ring-step kernel",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded N(0,1), rounded to bf16)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "global_seq": w.S,
+                   "ring_P": w.P, "rank": args.rank, "local_q": w.L, "split": w.split,
+                   "causal": w.causal, "prefetch": not args.no_prefetch,
+                   "parallelism": "one rank's share, ring simulated on 1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_DENSE / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_DENSE,
+                     "traffic": traffic, "kernel": "ra_step (step_mfma_kernel)",
+                     "kernel_ms_mean": k_mean_ms,
+                     "kernel_ms_per_ring_step": [float(x) for x in kms.mean(axis=0)],
+                     "flop_per_launch_mean": total / w.P},
+        "ring_ms_per_pass": ms_per_step,
+        "kernel_share_of_pass": float(kms.sum(axis=1).mean()) / ms_per_step,
+    }
+    if not args.no_legs:
+        log("[bench] legs: merge, factored spatial, factored temporal")
+        rec["legs"] = legs(w, q, dev, reps=20)
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle for ~{args.cpu_budget:.0f} s")
+        rec["cpu_baseline"] = cpu_baseline(w, args.rank, segs, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

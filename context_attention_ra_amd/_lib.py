@@ -1,0 +1,167 @@
+"""ctypes binding of libra.so: the C-ABI entry points under the same names.
+
+Argument marshalling only: shapes are read off the tensors, pointers and the
+stream handle are passed through, and a non-OK status raises. Every operation
+runs in the library's HIP kernels. If the library is missing the import of an
+entry point fails loudly; there is no fallback.
+"""
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libra.so")
+
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
+RA_F32, RA_BF16 = 0, 1
+RA_MASK_NONE, RA_MASK_CAUSAL = 0, 1
+RA_STEP_INIT = 1
+
+# every symbol include/ra.h declares
+EXPORTS = ("ra_step", "ra_finalize", "ra_merge_lse", "ra_factored_spatial",
+           "ra_factored_temporal", "ra_kv_pass", "ra_status_string",
+           "ra_last_hip_error", "ra_version")
+
+
+class RaSegs(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("start", ctypes.c_int64 * 2), ("len", ctypes.c_int64 * 2)]
+
+
+class RaError(RuntimeError):
+    def __init__(self, name, status, hip_error):
+        self.status = status
+        self.hip_error = hip_error
+        super().__init__(f"{name} failed: {status_name(status)} (hipError {hip_error})")
+
+
+_lib = None
+
+_vp, _i32, _f32, _u32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_uint32, ctypes.c_size_t
+_SIGS = {
+    "ra_step": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                       ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
+                       _vp, _vp, _vp, _vp]),
+    "ra_finalize": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "ra_merge_lse": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "ra_factored_spatial": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                   _vp, _vp, _vp]),
+    "ra_factored_temporal": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                    _vp, _vp, _vp]),
+    "ra_kv_pass": (_i32, [_vp, _vp, _vp, _vp, _sz, _vp]),
+    "ra_status_string": (ctypes.c_char_p, [_i32]),
+    "ra_last_hip_error": (_i32, []),
+    "ra_version": (_i32, []),
+}
+
+
+def load(path: str = LIB_PATH):
+    """Load libra.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m context_attention_ra_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_name(status: int) -> str:
+    return load().ra_status_string(status).decode()
+
+
+def _check(name: str, status: int):
+    if status != RA_OK:
+        raise RaError(name, status, load().ra_last_hip_error())
+
+
+def segs(runs: Sequence[Tuple[int, int]]) -> RaSegs:
+    """[(global start, length), ...] -> ra_segs (one or two runs)."""
+    s = RaSegs()
+    s.n = len(runs)
+    s.reserved = 0
+    for i, (st, n) in enumerate(runs[:2]):
+        s.start[i] = int(st)
+        s.len[i] = int(n)
+    return s
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libra must be contiguous")
+    return t.data_ptr()
+
+
+def _s(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def ra_step(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, init=False, stream=None):
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    qs, ks = segs(q_segs), segs(kv_segs)
+    st = load().ra_step(_p(q), _p(k), _p(v), _dtype(q), B, H, Lq, Lk, d,
+                        ctypes.byref(qs), ctypes.byref(ks),
+                        RA_MASK_CAUSAL if causal else RA_MASK_NONE, float(scale),
+                        RA_STEP_INIT if init else 0, _p(o_acc), _p(m), _p(l), _s(stream))
+    _check("ra_step", st)
+
+
+def ra_finalize(o_acc, m, l, out, lse=None, stream=None):
+    B, H, L, d = o_acc.shape
+    _check("ra_finalize", load().ra_finalize(_p(o_acc), _p(m), _p(l), B, H, L, d, _p(out),
+                                             _dtype(out), _p(lse), _s(stream)))
+
+
+def ra_merge_lse(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
+    B, H, L, d = o_a.shape
+    _check("ra_merge_lse", load().ra_merge_lse(_p(o_a), _p(lse_a), _p(o_b), _p(lse_b),
+                                               _dtype(o_a), B, H, L, d, _p(o_out),
+                                               _p(lse_out), _s(stream)))
+
+
+def ra_factored_spatial(q, k, v, T, S_sp, scale, out, lse=None, stream=None):
+    B, H, N, d = q.shape
+    if N != T * S_sp:
+        raise ValueError("q.shape[2] must equal T * S_sp")
+    _check("ra_factored_spatial", load().ra_factored_spatial(
+        _p(q), _p(k), _p(v), _dtype(q), B, H, T, S_sp, d, float(scale), _p(out), _p(lse), _s(stream)))
+
+
+def ra_factored_temporal(q, k, v, T, S_sp, scale, out, lse=None, stream=None):
+    B, H, N, d = q.shape
+    if N != T * S_sp:
+        raise ValueError("q.shape[2] must equal T * S_sp")
+    _check("ra_factored_temporal", load().ra_factored_temporal(
+        _p(q), _p(k), _p(v), _dtype(q), B, H, T, S_sp, d, float(scale), _p(out), _p(lse), _s(stream)))
+
+
+def ra_kv_pass(k_src, v_src, k_dst, v_dst, stream=None):
+    nbytes = k_src.numel() * k_src.element_size()
+    for t in (v_src, k_dst, v_dst):
+        if t.numel() * t.element_size() != nbytes:
+            raise ValueError("ra_kv_pass: all four buffers must have the same size")
+    _check("ra_kv_pass", load().ra_kv_pass(_p(k_src), _p(v_src), _p(k_dst), _p(v_dst),
+                                           nbytes, _s(stream)))

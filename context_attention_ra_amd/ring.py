@@ -1,0 +1,126 @@
+"""One rank's ring, simulated on one GPU: P block steps with a side-stream prefetch.
+
+Ring attention as the pages describe it (Day 83 post, "Context parallelism:
+splitting the sequence"; k8ai "How context parallel works", ring figure): the
+rank keeps its queries; at step s it holds the K/V block of rank (r - s) mod P,
+folds it into the running state with ``ra_step``, and meanwhile the block for
+step s+1 is being passed to it. Here every rank's block already sits in this
+GPU's memory, so the pass is ``ra_kv_pass`` (a device-to-device copy) enqueued
+on a side stream into one half of a double buffer, ordered against the compute
+stream with events exactly as a network receive would be. After the last step
+``ra_finalize`` writes the output and its log-sum-exp.
+
+This module is host control only: every byte of the path moves in libra.
+"""
+
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib, layout
+
+
+class RingState:
+    """The running (O_acc, m, l) state of one rank's queries (fp32)."""
+
+    def __init__(self, B, H, L, d, device):
+        self.o = torch.empty((B, H, L, d), dtype=torch.float32, device=device)
+        self.m = torch.empty((B, H, L), dtype=torch.float32, device=device)
+        self.l = torch.empty((B, H, L), dtype=torch.float32, device=device)
+
+
+def run(q: torch.Tensor,
+        q_segs: Sequence[Tuple[int, int]],
+        kv_blocks: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+        kv_segs: Sequence[Sequence[Tuple[int, int]]],
+        rank: int,
+        causal: bool,
+        scale: Optional[float] = None,
+        order: Optional[List[int]] = None,
+        prefetch: bool = True,
+        out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None,
+        state: Optional[RingState] = None,
+        bufs: Optional[List[Tuple[torch.Tensor, torch.Tensor]]] = None,
+        copy_stream: Optional[torch.cuda.Stream] = None,
+        step_events: Optional[List[Tuple[torch.cuda.Event, torch.cuda.Event]]] = None,
+        finalize: bool = True):
+    """Run rank `rank`'s share of ring attention on the current stream.
+
+    q          [B, H, Lq, d] local queries; q_segs their global positions
+    kv_blocks  P pairs (k_t, v_t), rank t's local K/V [B, H, Lk, d]
+    kv_segs    P segment lists, the global positions of each rank's block
+    order      source rank per step (default: the ring, (rank - s) mod P)
+    prefetch   True: pass the next block on `copy_stream` while the current
+               step computes; False: pass it on the compute stream first
+    returns (out [B, H, Lq, d] in q's dtype, lse [B, H, Lq] fp32, state)
+    """
+    P = len(kv_blocks)
+    if order is None:
+        order = layout.ring_order(rank, P)
+    if sorted(order) != list(range(P)):
+        raise ValueError("order must visit every block once")
+    B, H, Lq, d = q.shape
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    compute = torch.cuda.current_stream(dev)
+    if state is None:
+        state = RingState(B, H, Lq, d, dev)
+    if out is None and finalize:
+        out = torch.empty_like(q)
+    if lse is None and finalize:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+
+    needs_pass = [t != rank for t in order]
+    if any(needs_pass) and bufs is None:
+        k0, v0 = kv_blocks[0]
+        bufs = [(torch.empty_like(k0), torch.empty_like(v0)) for _ in range(2)]
+    if prefetch and any(needs_pass):
+        if copy_stream is None:
+            copy_stream = torch.cuda.Stream(dev)
+        copy_stream.wait_stream(compute)  # inputs written on the compute stream
+        for kb, vb in bufs:
+            kb.record_stream(copy_stream)
+            vb.record_stream(copy_stream)
+    ev_ready = [torch.cuda.Event(), torch.cuda.Event()]
+    ev_free = [torch.cuda.Event(), torch.cuda.Event()]
+    used = [False, False]
+
+    def pass_block(s):
+        slot = s % 2
+        src_k, src_v = kv_blocks[order[s]]
+        dst_k, dst_v = bufs[slot]
+        if prefetch:
+            if used[slot]:
+                copy_stream.wait_event(ev_free[slot])
+            _lib.ra_kv_pass(src_k, src_v, dst_k, dst_v, stream=copy_stream)
+            ev_ready[slot].record(copy_stream)
+        else:
+            _lib.ra_kv_pass(src_k, src_v, dst_k, dst_v, stream=compute)
+
+    if prefetch and needs_pass[0]:
+        pass_block(0)
+    for s in range(P):
+        if prefetch and s + 1 < P and needs_pass[s + 1]:
+            pass_block(s + 1)
+        if needs_pass[s]:
+            if prefetch:
+                compute.wait_event(ev_ready[s % 2])
+            else:
+                pass_block(s)
+            k, v = bufs[s % 2]
+        else:
+            k, v = kv_blocks[order[s]]
+        if step_events is not None:
+            step_events[s][0].record(compute)
+        _lib.ra_step(q, k, v, q_segs, kv_segs[order[s]], causal, scale,
+                     state.o, state.m, state.l, init=(s == 0), stream=compute)
+        if step_events is not None:
+            step_events[s][1].record(compute)
+        if needs_pass[s]:
+            ev_free[s % 2].record(compute)
+            used[s % 2] = True
+    if finalize:
+        _lib.ra_finalize(state.o, state.m, state.l, out, lse, stream=compute)
+    return out, lse, state

@@ -12,10 +12,17 @@ the float32 draws rounded to nearest even (torch's conversion); the oracle
 reads those exact bfloat16 values back as float64.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
 ROW_BLOCK = 1024
+
+# numpy's generators release the GIL while filling large arrays, so blocks are
+# drawn concurrently; the values do not depend on the thread count.
+_POOL = ThreadPoolExecutor(max_workers=max(1, min(16, len(os.sched_getaffinity(0)))))
 
 # tensor ids
 Q, K, V = 0, 1, 2
@@ -27,12 +34,15 @@ def normal_rows(wid, tid, b, h, r0, r1, d):
         return np.zeros((0, d), dtype=np.float32)
     out = np.empty((r1 - r0, d), dtype=np.float32)
     j0, j1 = r0 // ROW_BLOCK, (r1 - 1) // ROW_BLOCK
-    for j in range(j0, j1 + 1):
+
+    def fill(j):
         blk = np.random.default_rng([wid, tid, b, h, j]).standard_normal(
             (ROW_BLOCK, d), dtype=np.float32)
         a = max(r0, j * ROW_BLOCK)
         z = min(r1, (j + 1) * ROW_BLOCK)
         out[a - r0:z - r0] = blk[a - j * ROW_BLOCK:z - j * ROW_BLOCK]
+
+    list(_POOL.map(fill, range(j0, j1 + 1)))
     return out
 
 

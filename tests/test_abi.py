@@ -1,0 +1,129 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+declared entry point, and rejects bad arguments before any HIP call.
+
+The pointers used here are fake (never dereferenced): every call below fails
+validation on the host, which is the behaviour under test.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from context_attention_ra_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from context_attention_ra_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert _lib.status_name(0) == "RA_OK"
+    assert _lib.status_name(1) == "RA_ERR_INVALID_ARG"
+    assert _lib.status_name(2) == "RA_ERR_UNSUPPORTED"
+    assert _lib.status_name(3) == "RA_ERR_HIP"
+    assert lib.ra_version() >= 100
+    assert lib.ra_last_hip_error() == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never touched
+
+
+def ptr(i):
+    return FAKE * (i + 1) << 20  # far apart: no accidental overlap
+
+
+def step(lib, q=None, k=None, v=None, dt=1, B=1, H=1, Lq=64, Lk=64, d=128, qs=((0, 64),),
+         ks=((0, 64),), mask=1, scale=0.1, flags=1, o=None, m=None, l=None):
+    q = ptr(0) if q is None else q
+    k = ptr(1) if k is None else k
+    v = ptr(2) if v is None else v
+    o = ptr(3) if o is None else o
+    m = ptr(4) if m is None else m
+    l = ptr(5) if l is None else l
+    a, b = _lib.segs(list(qs)), _lib.segs(list(ks))
+    return lib.ra_step(q, k, v, dt, B, H, Lq, Lk, d, ctypes.byref(a), ctypes.byref(b), mask,
+                       scale, flags, o, m, l, None)
+
+
+INV, UNS = _lib.RA_ERR_INVALID_ARG, _lib.RA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), INV), (dict(k=0), INV), (dict(v=0), INV), (dict(o=0), INV), (dict(m=0), INV),
+    (dict(l=0), INV), (dict(B=0), INV), (dict(H=-1), INV), (dict(Lq=0, qs=()), INV),
+    (dict(Lk=-5), INV), (dict(dt=7), INV), (dict(mask=2), INV), (dict(scale=0.0), INV),
+    (dict(scale=float("inf")), INV), (dict(scale=float("nan")), INV), (dict(scale=-1.0), INV),
+    (dict(flags=2), INV), (dict(qs=((0, 63),)), INV), (dict(qs=((0, 32), (-4, 32))), INV),
+    (dict(ks=((0, 32), (100, 33))), INV), (dict(ks=((0, 0), (10, 64))), INV),
+    (dict(qs=((2**31 - 10, 64),)), INV), (dict(q=ptr(0) + 8), INV),
+    (dict(o=ptr(0)), INV),  # state overlapping the queries
+    (dict(m=ptr(3)), INV),  # m overlapping o_acc
+    (dict(d=96), UNS), (dict(d=256), UNS),
+])
+def test_step_rejects_bad_arguments(lib, kw, expect):
+    assert step(lib, **kw) == expect
+
+
+def test_segs_with_three_runs_is_rejected(lib):
+    s = _lib.RaSegs()
+    s.n = 3
+    t = _lib.segs([(0, 64)])
+    assert lib.ra_step(ptr(0), ptr(1), ptr(2), 1, 1, 1, 64, 64, 128, ctypes.byref(s),
+                       ctypes.byref(t), 1, 0.1, 0, ptr(3), ptr(4), ptr(5), None) == INV
+    s = _lib.segs([(0, 64)])
+    s.reserved = 1
+    assert lib.ra_step(ptr(0), ptr(1), ptr(2), 1, 1, 1, 64, 64, 128, ctypes.byref(s),
+                       ctypes.byref(t), 1, 0.1, 0, ptr(3), ptr(4), ptr(5), None) == INV
+
+
+def test_finalize_and_merge_validation(lib):
+    f = lib.ra_finalize
+    assert f(None, ptr(1), ptr(2), 1, 1, 64, 128, ptr(3), 1, ptr(4), None) == INV
+    assert f(ptr(0), ptr(1), ptr(2), 1, 1, 64, 128, ptr(0), 1, None, None) == INV  # out == state
+    assert f(ptr(0), ptr(1), ptr(2), 1, 1, 64, 128, ptr(3), 9, None, None) == INV
+    assert f(ptr(0), ptr(1), ptr(2), 1, 1, 64, 80, ptr(3), 1, None, None) == UNS
+    mg = lib.ra_merge_lse
+    assert mg(ptr(0), ptr(1), ptr(2), ptr(3), 1, 1, 1, 64, 128, None, ptr(5), None) == INV
+    # output partially overlapping an input is refused; exact aliasing is allowed (not launched here)
+    assert mg(ptr(0), ptr(1), ptr(2), ptr(3), 1, 1, 1, 64, 128, ptr(0) + 256, ptr(5), None) == INV
+    assert mg(ptr(0), ptr(1), ptr(2), ptr(3), 1, 1, 1, 64, 64 + 1, ptr(4), ptr(5), None) == UNS
+
+
+def test_factored_validation(lib):
+    for fn in (lib.ra_factored_spatial, lib.ra_factored_temporal):
+        assert fn(None, ptr(1), ptr(2), 1, 1, 1, 4, 9, 128, 0.1, ptr(3), None, None) == INV
+        assert fn(ptr(0), ptr(1), ptr(2), 1, 1, 1, 0, 9, 128, 0.1, ptr(3), None, None) == INV
+        assert fn(ptr(0), ptr(1), ptr(2), 1, 1, 1, 4, 9, 128, 0.1, ptr(1), None, None) == INV
+        assert fn(ptr(0), ptr(1), ptr(2), 0, 1, 1, 4, 9, 128, 0.1, ptr(3), None, None) == UNS
+        assert fn(ptr(0), ptr(1), ptr(2), 1, 1, 1, 4, 9, 32, 0.1, ptr(3), None, None) == UNS
+    assert lib.ra_factored_temporal(ptr(0), ptr(1), ptr(2), 1, 1, 1, 17, 9, 128, 0.1, ptr(3),
+                                    None, None) == UNS
+
+
+def test_kv_pass_validation(lib):
+    assert lib.ra_kv_pass(ptr(0), ptr(1), ptr(2), ptr(3), 0, None) == _lib.RA_OK  # no-op
+    assert lib.ra_kv_pass(None, ptr(1), ptr(2), ptr(3), 64, None) == INV
+    assert lib.ra_kv_pass(ptr(0), ptr(1), ptr(0), ptr(3), 64, None) == INV
+    assert lib.ra_kv_pass(ptr(0), ptr(1), ptr(2), ptr(2) + 32, 64, None) == INV

@@ -1,0 +1,354 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case prints its name and shape before touching the GPU. Tolerances are
+the ones stated for the method's outputs (see ringcase.TOL).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded
+from context_attention_ra_amd import _lib, configs, ring
+from ringcase import RingCase, assert_close, compare, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def run_case(case, **kw):
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, case.rank, case.w.causal,
+                           scale=case.w.scale, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("rank", [0, 1, 2, 3])
+def test_tiny_f32_ring(gpu_lib, rank):
+    w = configs.TINY_F32
+    banner(f"{w.name} rank {rank}")
+    case = RingCase(w, rank)
+    out, lse = run_case(case)
+    ro, rl = case.expected()
+    assert_close(out.cpu().double().numpy(), ro, lse.cpu().double().numpy(), rl, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_causal_2rank_full(gpu_lib, rank):
+    w = configs.CAUSAL_2RANK
+    banner(f"{w.name} rank {rank}")
+    case = RingCase(w, rank)
+    out, lse = run_case(case)
+    ro, rl = case.expected()
+    assert_close(out.float().cpu().double().numpy(), ro, lse.cpu().double().numpy(), rl, w.dtype, w.name)
+
+
+def _sampled(w, rank, **kw):
+    banner(f"{w.name} rank {rank} (sampled rows)")
+    case = RingCase(w, rank)
+    out, lse = run_case(case, **kw)
+    rows = sample_rows(w, rank)
+    ro, rl = case.expected(rows)
+    idx = torch.as_tensor(rows, device=out.device)
+    go = out.index_select(2, idx).float().cpu().double().numpy()
+    gl = lse.index_select(2, idx).cpu().double().numpy()
+    assert_close(go, ro, gl, rl, w.dtype, f"{w.name} r{rank} {rows.size} rows/head")
+    # properties that hold for every row: finite output, finite lse
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    return case, out, lse
+
+
+def test_llm_32k_rank0_sampled(gpu_lib):
+    _sampled(configs.LLM_32K_CP4, 0)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("rank", [1, 2, 3])
+def test_llm_32k_other_ranks_sampled(gpu_lib, rank):
+    _sampled(configs.LLM_32K_CP4, rank)
+
+
+@pytest.mark.slow
+def test_video_dit_432k_sampled(gpu_lib):
+    _sampled(configs.VIDEO_DIT_CP8, 3)
+
+
+def _video_inputs(v, device="cuda"):
+    qkv = [seeded.gen_bhsd(v.wid, tid, v.B, v.H, 0, v.N, v.d, v.dtype, device)
+           for tid in (seeded.Q, seeded.K, seeded.V)]
+    return qkv
+
+
+@pytest.mark.parametrize("kind", ["spatial", "temporal"])
+def test_video_factored_full(gpu_lib, kind):
+    v = configs.VIDEO_FACTORED
+    banner(f"{v.name} {kind}")
+    q, k, vv = _video_inputs(v)
+    out = torch.empty_like(q)
+    lse = torch.empty((v.B, v.H, v.N), dtype=torch.float32, device=q.device)
+    fn = _lib.ra_factored_spatial if kind == "spatial" else _lib.ra_factored_temporal
+    fn(q, k, vv, v.T, v.S_sp, v.scale, out, lse)
+    torch.cuda.synchronize()
+    ofn = oracle.factored_spatial if kind == "spatial" else oracle.factored_temporal
+    ro = np.zeros((v.B, v.H, v.N, v.d))
+    rl = np.zeros((v.B, v.H, v.N))
+    qc, kc, vc = (seeded.exact_f64(t.cpu()) for t in (q, k, vv))
+    for b in range(v.B):
+        for h in range(v.H):
+            ro[b, h], rl[b, h] = ofn(qc[b, h], kc[b, h], vc[b, h], v.T, v.S_sp, v.scale)
+    assert_close(out.float().cpu().double().numpy(), ro, lse.cpu().double().numpy(), rl, v.dtype,
+                 f"{v.name} {kind}")
+
+
+@pytest.mark.parametrize("kind", ["spatial", "temporal"])
+@pytest.mark.parametrize("d,T,S_sp", [(64, 5, 37), (128, 16, 7), (128, 3, 130), (64, 16, 257)])
+def test_factored_ragged(gpu_lib, kind, d, T, S_sp):
+    banner(f"factored {kind} d={d} T={T} S_sp={S_sp}")
+    B, H = 2, 3
+    N = T * S_sp
+    q, k, v = (seeded.gen_bhsd(90 + d, tid, B, H, 0, N, d, torch.bfloat16, "cuda") for tid in range(3))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    scale = d ** -0.5
+    fn = _lib.ra_factored_spatial if kind == "spatial" else _lib.ra_factored_temporal
+    fn(q, k, v, T, S_sp, scale, out, lse)
+    torch.cuda.synchronize()
+    ofn = oracle.factored_spatial if kind == "spatial" else oracle.factored_temporal
+    qc, kc, vc = (seeded.exact_f64(t.cpu()) for t in (q, k, v))
+    ro = np.zeros((B, H, N, d))
+    rl = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            ro[b, h], rl[b, h] = ofn(qc[b, h], kc[b, h], vc[b, h], T, S_sp, scale)
+    assert_close(out.float().cpu().double().numpy(), ro, lse.cpu().double().numpy(), rl,
+                 torch.bfloat16, f"{kind} d{d} T{T} S{S_sp}")
+
+
+# ---- single-step cases with ragged tails and arbitrary segment tables ---------
+
+STEP_CASES = [
+    # (B, H, Lq, q_runs, Lk, k_runs, d, causal, dtype)
+    (1, 1, 128, [(0, 128)], 64, [(0, 64)], 128, False, torch.bfloat16),
+    (2, 3, 300, [(0, 300)], 200, [(100, 200)], 128, True, torch.bfloat16),
+    (2, 3, 300, [(40, 137), (1000, 163)], 333, [(0, 250), (900, 83)], 128, True, torch.bfloat16),
+    (1, 2, 517, [(0, 517)], 999, [(0, 999)], 64, False, torch.bfloat16),
+    (1, 2, 257, [(500, 129), (2000, 128)], 700, [(300, 350), (1900, 350)], 64, True, torch.bfloat16),
+    (2, 2, 190, [(64, 190)], 161, [(0, 161)], 64, True, torch.float32),
+    (1, 3, 77, [(10, 40), (300, 37)], 250, [(0, 120), (200, 130)], 128, True, torch.float32),
+    (1, 1, 96, [(0, 96)], 33, [(5, 33)], 128, False, torch.float32),
+]
+
+
+def _runs_pos(runs):
+    return np.concatenate([np.arange(s, s + n) for s, n in runs])
+
+
+@pytest.mark.parametrize("ci", range(len(STEP_CASES)))
+def test_single_step_ragged(gpu_lib, ci):
+    B, H, Lq, qr, Lk, kr, d, causal, dt = STEP_CASES[ci]
+    banner(f"step case {ci}: B{B} H{H} Lq{Lq} Lk{Lk} d{d} causal={causal} {dt}")
+    q = seeded.gen_bhsd(70 + ci, 0, B, H, 0, Lq, d, dt, "cuda")
+    k = seeded.gen_bhsd(70 + ci, 1, B, H, 0, Lk, d, dt, "cuda")
+    v = seeded.gen_bhsd(70 + ci, 2, B, H, 0, Lk, d, dt, "cuda")
+    st = ring.RingState(B, H, Lq, d, "cuda")
+    scale = d ** -0.5
+    _lib.ra_step(q, k, v, qr, kr, causal, scale, st.o, st.m, st.l, init=True)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    _lib.ra_finalize(st.o, st.m, st.l, out, lse)
+    torch.cuda.synchronize()
+    qp, kp = _runs_pos(qr), _runs_pos(kr)
+    qc, kc, vc = (seeded.exact_f64(t.cpu()) for t in (q, k, v))
+    ro = np.zeros((B, H, Lq, d))
+    rl = np.zeros((B, H, Lq))
+    for b in range(B):
+        for h in range(H):
+            ro[b, h], rl[b, h] = oracle.attention_rows(qc[b, h], qp, kc[b, h], vc[b, h], kp, scale, causal)
+    go, gl = out.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    empty = ~np.isfinite(rl)
+    assert np.array_equal(empty, ~np.isfinite(gl)), "rows without visible keys must give lse = -inf"
+    assert np.all(go[empty] == 0.0)
+    rl_f = np.where(empty, 0.0, rl)
+    gl_f = np.where(empty, 0.0, gl)
+    assert_close(go, ro, gl_f, rl_f, dt, f"step case {ci}")
+
+
+def test_rows_without_visible_keys(gpu_lib):
+    banner("causal rows that see no key: out = 0, lse = -inf, state untouched")
+    d, B, H = 128, 1, 2
+    q = seeded.gen_bhsd(81, 0, B, H, 0, 64, d, torch.bfloat16, "cuda")
+    k = seeded.gen_bhsd(81, 1, B, H, 0, 128, d, torch.bfloat16, "cuda")
+    v = seeded.gen_bhsd(81, 2, B, H, 0, 128, d, torch.bfloat16, "cuda")
+    st = ring.RingState(B, H, 64, d, "cuda")
+    # queries at positions 0..63, keys at 1000.. : nothing visible
+    _lib.ra_step(q, k, v, [(0, 64)], [(1000, 128)], True, d ** -0.5, st.o, st.m, st.l, init=True)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, 64), dtype=torch.float32, device="cuda")
+    _lib.ra_finalize(st.o, st.m, st.l, out, lse)
+    torch.cuda.synchronize()
+    assert torch.all(st.l == 0) and torch.all(st.o == 0) and torch.all(torch.isneginf(st.m))
+    assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+# ---- invariants on the GPU --------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def c2_case(gpu_lib):
+    return RingCase(configs.CAUSAL_2RANK, 0)
+
+
+def test_block_order_independence(c2_case):
+    banner("block order: ring order vs reversed (causal 4k, P=2) and 4-block orders")
+    w = c2_case.w
+    o1, l1 = run_case(c2_case)
+    o2, l2 = run_case(c2_case, order=[1, 0])
+    ro, rl = c2_case.expected()
+    for o, l, name in ((o1, l1, "ring"), (o2, l2, "reversed")):
+        assert_close(o.float().cpu().double().numpy(), ro, l.cpu().double().numpy(), rl, w.dtype, name)
+
+
+@pytest.mark.parametrize("order", [[2, 1, 0, 3], [3, 2, 1, 0], [0, 3, 1, 2]])
+def test_tiny_f32_any_order(gpu_lib, order):
+    w = configs.TINY_F32
+    banner(f"{w.name} rank 2 order {order}")
+    case = RingCase(w, 2)
+    out, lse = run_case(case, order=order)
+    ro, rl = case.expected()
+    assert_close(out.cpu().double().numpy(), ro, lse.cpu().double().numpy(), rl, w.dtype, str(order))
+
+
+def test_running_state_equals_merge_of_partials(c2_case):
+    banner("running state vs per-step partials merged with ra_merge_lse")
+    case = c2_case
+    w = case.w
+    order = [0, 1]
+    parts = []
+    for t in order:
+        st = ring.RingState(w.B, w.H, w.L, w.d, "cuda")
+        k, v = case.kv[t]
+        _lib.ra_step(case.q, k, v, case.q_segs, case.kv_segs[t], True, w.scale, st.o, st.m, st.l, init=True)
+        o = torch.empty_like(case.q)
+        lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device="cuda")
+        _lib.ra_finalize(st.o, st.m, st.l, o, lse)
+        parts.append((o, lse))
+    om = torch.empty_like(case.q)
+    lm = torch.empty_like(parts[0][1])
+    _lib.ra_merge_lse(parts[0][0], parts[0][1], parts[1][0], parts[1][1], om, lm)
+    torch.cuda.synchronize()
+    ro, rl = case.expected()
+    assert_close(om.float().cpu().double().numpy(), ro, lm.cpu().double().numpy(), rl, w.dtype, "merged")
+
+
+def test_init_flag_equals_explicit_empty_state(c2_case):
+    banner("RA_STEP_INIT vs an explicit (0, -inf, 0) state: bitwise")
+    case, w = c2_case, c2_case.w
+    k, v = case.kv[0]
+    a = ring.RingState(w.B, w.H, w.L, w.d, "cuda")
+    b = ring.RingState(w.B, w.H, w.L, w.d, "cuda")
+    _lib.ra_step(case.q, k, v, case.q_segs, case.kv_segs[0], True, w.scale, a.o, a.m, a.l, init=True)
+    b.o.zero_()
+    b.m.fill_(float("-inf"))
+    b.l.zero_()
+    _lib.ra_step(case.q, k, v, case.q_segs, case.kv_segs[0], True, w.scale, b.o, b.m, b.l, init=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a.o, b.o) and torch.equal(a.m, b.m) and torch.equal(a.l, b.l)
+
+
+def test_deterministic_and_prefetch_modes_bitwise(c2_case):
+    banner("run-to-run determinism; prefetch vs serial pass; delayed side stream")
+    o1, l1 = run_case(c2_case)
+    o2, l2 = run_case(c2_case)
+    o3, l3 = run_case(c2_case, prefetch=False)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    # a copy stream held back by a spin kernel must not change the result
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(50_000_000)
+    o4, l4, _ = ring.run(c2_case.q, c2_case.q_segs, c2_case.kv, c2_case.kv_segs, 1, True,
+                         scale=c2_case.w.scale, copy_stream=side)
+    torch.cuda.synchronize()
+    o5, l5, _ = ring.run(c2_case.q, c2_case.q_segs, c2_case.kv, c2_case.kv_segs, 1, True,
+                         scale=c2_case.w.scale, prefetch=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o4, o5) and torch.equal(l4, l5)
+
+
+def test_checkpoint_resume_bitwise(gpu_lib):
+    banner("checkpoint the state after step 1, resume: bitwise equal")
+    case = RingCase(configs.TINY_F32, 0)
+    w = case.w
+    full_o, full_l, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, 0, False, scale=w.scale)
+    order = [0, 3, 2, 1]
+    st = ring.RingState(w.B, w.H, w.L, w.d, "cuda")
+    for s in range(2):
+        k, v = case.kv[order[s]]
+        _lib.ra_step(case.q, k, v, case.q_segs, case.kv_segs[order[s]], False, w.scale, st.o, st.m, st.l, init=s == 0)
+    saved = [x.clone() for x in (st.o, st.m, st.l)]
+    st2 = ring.RingState(w.B, w.H, w.L, w.d, "cuda")
+    st2.o.copy_(saved[0]), st2.m.copy_(saved[1]), st2.l.copy_(saved[2])
+    for s in range(2, 4):
+        k, v = case.kv[order[s]]
+        _lib.ra_step(case.q, k, v, case.q_segs, case.kv_segs[order[s]], False, w.scale, st2.o, st2.m, st2.l)
+    out = torch.empty_like(case.q)
+    lse = torch.empty_like(full_l)
+    _lib.ra_finalize(st2.o, st2.m, st2.l, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, full_o) and torch.equal(lse, full_l)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_lse_parity(gpu_lib, dt, d):
+    banner(f"ra_merge_lse {dt} d={d}, with empty rows and in-place output")
+    B, H, L = 2, 3, 333
+    oa = seeded.gen_bhsd(60, 0, B, H, 0, L, d, dt, "cuda")
+    ob = seeded.gen_bhsd(60, 1, B, H, 0, L, d, dt, "cuda")
+    la = (3.0 * seeded.gen_bhsd(60, 2, B, H, 0, L, 1, torch.float32, "cuda"))[..., 0].contiguous()
+    lb = (3.0 * seeded.gen_bhsd(60, 3, B, H, 0, L, 1, torch.float32, "cuda"))[..., 0].contiguous()
+    la[:, :, :7] = float("-inf")
+    lb[:, :, 3:11] = float("-inf")
+    oa[:, :, :7] = 0
+    ob[:, :, 3:11] = 0
+    ref_o, ref_l = [], []
+    oac, obc, lac, lbc = (seeded.exact_f64(t.cpu()) for t in (oa, ob, la, lb))
+    ro = np.zeros((B, H, L, d))
+    rl = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            ro[b, h], rl[b, h] = oracle.merge_lse(oac[b, h], lac[b, h], obc[b, h], lbc[b, h])
+    oo = torch.empty_like(oa)
+    lo = torch.empty_like(la)
+    _lib.ra_merge_lse(oa, la, ob, lb, oo, lo)
+    _lib.ra_merge_lse(oa, la, ob, lb, oa, la)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(oo, oa) and torch.equal(lo, la)
+    go, gl = oo.float().cpu().double().numpy(), lo.cpu().double().numpy()
+    both = ~np.isfinite(rl)
+    assert np.array_equal(both, ~np.isfinite(gl))
+    tol = 2e-2 if dt == torch.bfloat16 else 1e-5
+    mx, mr = compare(go, ro)
+    lm, _ = compare(np.where(both, 0, gl), np.where(both, 0, rl))
+    print(f"merge {dt} d{d}: max_abs={mx:.3e} mean_rel={mr:.3e} lse={lm:.3e}", flush=True)
+    assert mx <= tol and lm <= 1e-5
+
+
+def test_invalid_arguments_raise_before_launch(gpu_lib):
+    banner("argument errors are reported, nothing launched")
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
+    st = ring.RingState(1, 1, 64, 128, "cuda")
+    with pytest.raises(_lib.RaError) as e:
+        _lib.ra_step(q, q, q, [(0, 63)], [(0, 64)], True, 0.1, st.o, st.m, st.l, init=True)
+    assert e.value.status == _lib.RA_ERR_INVALID_ARG
+    with pytest.raises(_lib.RaError) as e:
+        _lib.ra_step(q, q, q, [(0, 64)], [(0, 64)], True, float("nan"), st.o, st.m, st.l)
+    assert e.value.status == _lib.RA_ERR_INVALID_ARG
+    q96 = torch.zeros((1, 1, 64, 96), dtype=torch.bfloat16, device="cuda")
+    st96 = ring.RingState(1, 1, 64, 96, "cuda")
+    with pytest.raises(_lib.RaError) as e:
+        _lib.ra_step(q96, q96, q96, [(0, 64)], [(0, 64)], True, 0.1, st96.o, st96.m, st96.l)
+    assert e.value.status == _lib.RA_ERR_UNSUPPORTED
