@@ -80,6 +80,8 @@ ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt, int3
   if (!supported_d(d)) return RA_ERR_UNSUPPORTED;
   const int64_t tiles = (int64_t)nb * ((Lq + 127) / 128);
   if (tiles > (int64_t)INT32_MAX / 2) return RA_ERR_UNSUPPORTED;
+  // one (batch, head) slice of K or V must be addressable by a 32-bit offset
+  if ((int64_t)Lk * d * (int64_t)es > (int64_t)INT32_MAX) return RA_ERR_UNSUPPORTED;
 
   ra::StepArgs a{};
   a.q = q;

@@ -9,23 +9,33 @@
 // the k8ai page needs no special casing here.
 //
 // Design (CDNA4-first; FlashAttention is prior art, not the template):
-// * A workgroup is 4 waves; each wave owns 32 query rows, so a workgroup
-//   covers 128 rows. Keys stream through LDS in tiles of 64 rows, double
-//   buffered: the next tile is fetched into registers with 16-byte loads while
-//   the current one is consumed, then written to the other LDS buffer.
+// * A workgroup is kWaves waves and each wave owns 32*kQB query rows. With
+//   two 32-row blocks per wave every K or V fragment a wave reads from LDS
+//   feeds two MFMAs, which halves LDS traffic per FLOP: on gfx950 the
+//   transposed LDS read runs at about half the rate of a plain 16-byte read
+//   and would otherwise rival the matrix-core time.
+// * Keys stream through a kStages-deep LDS ring in tiles of kBK rows, fetched
+//   by bounds-checked buffer loads that write LDS directly (no staging
+//   registers; rows past the block read as zero). A tile is requested
+//   kStages-1 iterations before it is consumed and waited for only just
+//   before, so global latency hides behind several iterations; one barrier
+//   per tile.
+// * LDS holds each tile column-major in 16-byte columns; one load instruction
+//   fills a 1 KiB run (one or two columns), runs padded to 1088 bytes. Both the
+//   16-byte K reads and the transposed V reads are then free of bank
+//   conflicts, and every LDS address is a per-lane base plus an immediate.
 // * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //   the 32x32 accumulator layout gives every lane one query column and 16 of
-//   the 32 keys, so a row maximum is an in-lane reduction plus one 32-lane swap
-//   (v_permlane32_swap), and the per-query rescale factor is a lane scalar.
+//   each 32 keys, so a row maximum is an in-lane reduction plus one 32-lane
+//   swap (v_permlane32_swap), and the per-query rescale factor is a lane scalar.
+// * Software pipelining inside each wave: the score MFMAs of tile n+1 are
+//   issued next to the exponentials of tile n, and the PV MFMAs of tile n next
+//   to the row maximum of tile n+1, so matrix core and vector ALUs overlap.
 // * The probabilities stay in registers as the B operand of O^T += V^T P^T.
 //   The key order inside each 16-key MFMA slice is permuted to match the
 //   accumulator layout; the matching V^T operand is read with the gfx950
-//   transposing LDS load ds_read_b64_tr_b16, so no LDS round trip of P and no
-//   shuffles are needed.
-// * LDS rows are XOR-swizzled in 16-byte chunks (different patterns for K and
-//   V) so that both the 16-byte K reads and the transposed V reads are free
-//   of bank conflicts.
-// * The running maximum is only moved when a tile's maximum exceeds it by more
+//   transposing LDS load ds_read_b64_tr_b16, so P never leaves registers.
+// * The running maximum only moves when a tile's maximum exceeds it by more
 //   than 2^8 in weight (lazy rescale); the state stays exact because O and l
 //   are always expressed relative to the same reference value m.
 // * Tiles whose keys all lie after the last query (causal) are never loaded;
@@ -38,53 +48,90 @@
 #include "ra_device.h"
 #include "ra_launch.h"
 
+#ifndef RA_STEP_WAVES
+#define RA_STEP_WAVES 8
+#endif
+#ifndef RA_STEP_QBLOCKS
+#define RA_STEP_QBLOCKS 1
+#endif
+#ifndef RA_STEP_BK
+#define RA_STEP_BK 64
+#endif
+#ifndef RA_STEP_STAGES
+#define RA_STEP_STAGES 4
+#endif
+#ifndef RA_STEP_PINGPONG
+#define RA_STEP_PINGPONG 1
+#endif
+#ifndef RA_STEP_GROUP_ODD
+#define RA_STEP_GROUP_ODD 0
+#endif
+#ifndef RA_STEP_LDS_AHEAD
+#define RA_STEP_LDS_AHEAD 3
+#endif
+
 namespace ra {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = RA_STEP_WAVES;   // waves per workgroup
+constexpr int kQB = RA_STEP_QBLOCKS;    // 32-row query blocks per wave
+constexpr int kBK = RA_STEP_BK;         // key rows per tile (32 or 64)
+constexpr int kStages = RA_STEP_STAGES; // LDS ring depth
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBQ = 32 * kWaves;  // query rows per workgroup
-constexpr int kBK = 64;           // key rows per tile
-constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
+constexpr int kBQ = 32 * kQB * kWaves;  // query rows per workgroup
+constexpr int kNST = kBK / 32;          // 32-key halves per tile
+constexpr int kRun = 1088;              // LDS bytes per 1 KiB load run, padded
+constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+static_assert(kBK == 32 || kBK == 64, "tile of 32 or 64 keys");
 
-// XOR swizzle of the 16-byte chunk `c` of LDS row `row`.
 template <int D>
-struct Swz;
-template <>
-struct Swz<128> {
-  static __device__ __forceinline__ int k(int row, int c) { return c ^ (row & 15); }
-  static __device__ __forceinline__ int v(int row, int c) {
-    return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
-  }
-};
-template <>
-struct Swz<64> {
-  static __device__ __forceinline__ int k(int row, int c) { return c ^ ((row >> 1) & 7); }
-  static __device__ __forceinline__ int v(int row, int c) {
-    return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
-  }
+struct Lay {
+  static constexpr int CPR = D / 8;               // 16-byte columns per row
+  static constexpr int COLS_PER_RUN = 64 / kBK;   // columns one load instruction fills
+  static constexpr int NRUN = CPR / COLS_PER_RUN; // runs per tensor tile
+  static constexpr int TBYTES = NRUN * kRun;      // one tensor's tile in LDS
+  static constexpr int STAGE = 2 * TBYTES;        // K tile then V tile
+  static constexpr int RUNS_PER_WAVE = NRUN / kWaves;
+  static_assert(RUNS_PER_WAVE >= 1 && NRUN % kWaves == 0, "runs must split evenly over waves");
+  static_assert(NRUN % 4 == 0, "layout assumes at least four runs");
+  // byte offset of (row, column) inside a tensor tile
+  static constexpr int at(int row, int col) { return (col % NRUN) * kRun + (col / NRUN) * 16 * kBK + 16 * row; }
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) char lds_char;
 
-template <int D>
-struct Tile {
-  static constexpr int kChunksPerRow = D / 8;                      // 16-byte chunks
-  static constexpr int kChunks = kBK * kChunksPerRow;              // per tensor
-  static constexpr int kPerThread = kChunks / kThreads;            // 4 (D=128) or 2
-};
+// 16 bytes per lane from a bounds-checked buffer straight into LDS at
+// m0 + 16*lane (gfx950 buffer_load_dwordx4 ... lds). Written as inline asm so
+// that the compiler does not treat these loads as pending LDS writes: it would
+// otherwise wait for every one of them before each transposed LDS read. The
+// kernel orders them itself with explicit vmcnt waits before its barriers.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, const char* lds, int voff,
+                                           int soff) {
+  const unsigned m0 = (unsigned)(size_t)(const lds_char*)lds;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
+               : "memory");
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(const char* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ bf16x4 lds_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// s_waitcnt encodings (gfx9): wait until at most N vector-memory ops are pending
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int D, bool CAUSAL, bool FUSED>
-__global__ __launch_bounds__(kThreads, 2) void step_mfma_kernel(
+__global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, int32_t init,
     float* __restrict__ Oacc, float* __restrict__ Mst, float* __restrict__ Lst,
     bf16* __restrict__ Out, float* __restrict__ Lse, int32_t nqt, int32_t per_xcd) {
-  constexpr int CPR = Tile<D>::kChunksPerRow;
-  constexpr int NPT = Tile<D>::kPerThread;
+  using L = Lay<D>;
   constexpr int KS = D / 16;  // k-steps of the score MFMA
   constexpr int DT = D / 32;  // 32-wide output tiles
-  __shared__ bf16x8 smem[2][2][Tile<D>::kChunks];  // [buffer][K/V][row*CPR + chunk]
+  constexpr int NDMA = 2 * L::RUNS_PER_WAVE;  // load instructions per wave per tile
+  __shared__ __attribute__((aligned(16))) char smem[kStages * L::STAGE];
 
   // ---- which (slice, query tile) this workgroup owns
   const int32_t total = nb * nqt;
@@ -100,49 +147,23 @@ __global__ __launch_bounds__(kThreads, 2) void step_mfma_kernel(
   const size_t qbase = (size_t)prob * Lq * D;
   const size_t kbase = (size_t)prob * Lk * D;
 
-  const int32_t qrow = qt0 + 32 * w + l32;
-  const bool qvalid = qrow < Lq;
-  const int32_t qrow_c = qvalid ? qrow : Lq - 1;
-  const int32_t qpos = seg_pos(qs, qrow_c);
+  // this wave's query rows: block b covers rows w_r0 + 32b .. +31
+  const int32_t w_r0 = qt0 + 32 * kQB * w;
+  int32_t qrow[kQB], qpos[kQB];
+  bool qvalid[kQB];
+#pragma unroll
+  for (int b = 0; b < kQB; ++b) {
+    qrow[b] = w_r0 + 32 * b + l32;
+    qvalid[b] = qrow[b] < Lq;
+    qpos[b] = seg_pos(qs, qvalid[b] ? qrow[b] : Lq - 1);
+  }
 
   const int32_t wg_r1 = min(qt0 + kBQ, Lq);
   int32_t wg_qlo, wg_qhi;
   seg_range(qs, qt0, wg_r1, wg_qlo, wg_qhi);
-  const int32_t w_r0 = qt0 + 32 * w;
   const bool wave_active = w_r0 < Lq;
   int32_t w_qlo = 0, w_qhi = -1;
-  if (wave_active) seg_range(qs, w_r0, min(w_r0 + 32, Lq), w_qlo, w_qhi);
-
-  // ---- query fragments: B operand of S^T = K Q^T (lane: query l32, d 16ks+8h..+8)
-  bf16x8 qf[KS];
-  {
-    const bf16* qp = Q + qbase + (size_t)qrow_c * D + 8 * h;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
-  }
-
-  // ---- running state: O^T accumulators (lane: query l32, d 32dt+8i+4h+j)
-  f32x16 o[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) o[t] = f32x16{};
-  float mu = kNegInf;  // reference value in log2 units of the weights
-  float lrun = 0.f;    // this lane's share of the row sum
-  if (!FUSED && !init && qvalid) {
-    const float* op = Oacc + qbase + (size_t)qrow * D + 4 * h;
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 x = *(const f32x4*)(op + 32 * t + 8 * i);
-        o[t][4 * i + 0] = x[0];
-        o[t][4 * i + 1] = x[1];
-        o[t][4 * i + 2] = x[2];
-        o[t][4 * i + 3] = x[3];
-      }
-    const size_t r = (size_t)prob * Lq + qrow;
-    mu = Mst[r] * kLog2e;
-    lrun = h == 0 ? Lst[r] : 0.f;
-  }
+  if (wave_active) seg_range(qs, w_r0, min(w_r0 + 32 * kQB, Lq), w_qlo, w_qhi);
 
   // ---- key rows this workgroup can see: at most two row ranges
   int32_t ra0 = 0, rb0 = Lk, ra1 = 0, rb1 = 0;
@@ -151,7 +172,6 @@ __global__ __launch_bounds__(kThreads, 2) void step_mfma_kernel(
       int32_t x = wg_qhi - start + 1;
       return x < 0 ? 0 : (x > n ? n : x);
     };
-    ra0 = 0;
     rb0 = vis(ks.start0, ks.len0);
     ra1 = ks.len0;
     rb1 = ks.len0 + (ks.len > ks.len0 ? vis(ks.start1, ks.len - ks.len0) : 0);
@@ -163,167 +183,440 @@ __global__ __launch_bounds__(kThreads, 2) void step_mfma_kernel(
   if (n0 > 0 && t1a < t0b) t1a = t0b;
   const int32_t n1 = rb1 > ra1 && t1b > t1a ? t1b - t1a : 0;
   const int32_t ntiles = n0 + n1;
-  auto tile_of = [&](int32_t n) { return n < n0 ? t0a + n : t1a + (n - n0); };
+  auto tile_kt0 = [&](int32_t n) { return (n < n0 ? t0a + n : t1a + (n - n0)) * kBK; };
 
-  u32x4 pk[NPT], pv[NPT];
-  auto gload = [&](int32_t kt0) {
+  // ---- K/V tiles: bounds-checked buffer loads straight into LDS. Load run r
+  // of a tile holds columns r, r+NRUN, ... of rows 0..kBK-1; lane i brings
+  // row i % kBK of column r + NRUN * (i / kBK). A wave owns RUNS_PER_WAVE runs.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), 0, Lk * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + kbase), 0, Lk * D * 2, 0x00020000);
+  auto fetch = [&](int32_t n, int stage) {
+    const int32_t soff = tile_kt0(n) * D * 2;
+    char* sb = smem + stage * L::STAGE;
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id / CPR, c = id % CPR;
-      const int32_t kr = kt0 + row;
-      if (kr < Lk) {
-        const size_t off = kbase + (size_t)kr * D + 8 * c;
-        pk[i] = *(const u32x4*)(K + off);
-        pv[i] = *(const u32x4*)(V + off);
-      } else {
-        pk[i] = u32x4{0, 0, 0, 0};
-        pv[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id / CPR, c = id % CPR;
-      *(u32x4*)&smem[buf][0][row * CPR + Swz<D>::k(row, c)] = pk[i];
-      *(u32x4*)&smem[buf][1][row * CPR + Swz<D>::v(row, c)] = pv[i];
+    for (int i = 0; i < L::RUNS_PER_WAVE; ++i) {
+      const int r = w * L::RUNS_PER_WAVE + i;
+      const int voff = (lane % kBK) * D * 2 + 16 * (r + L::NRUN * (lane / kBK));
+      load_lds16(krs, sb + r * kRun, voff, soff);
+      load_lds16(vrs, sb + L::TBYTES + r * kRun, voff, soff);
     }
   };
 
-  if (ntiles > 0) {
-    gload(tile_of(0) * kBK);
-    sstore(0);
-    __syncthreads();
+  // the first tiles are requested before the Q and state loads
+  constexpr int kPrologueTiles = RA_STEP_PINGPONG ? kStages : kStages - 1;
+#pragma unroll
+  for (int i = 0; i < kPrologueTiles; ++i)
+    if (ntiles > i) fetch(i, i);
+
+  // ---- query fragments: B operand of S^T = K Q^T (lane: query l32, d 16ks+8h..+8)
+  bf16x8 qf[kQB][KS];
+#pragma unroll
+  for (int b = 0; b < kQB; ++b) {
+    const bf16* qp = Q + qbase + (size_t)(qvalid[b] ? qrow[b] : Lq - 1) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[b][s] = *(const bf16x8*)(qp + 16 * s);
   }
 
-  for (int32_t n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
-    const int32_t kt0 = tile_of(n) * kBK;
-    const bool has_next = n + 1 < ntiles;
-    if (has_next) gload(tile_of(n + 1) * kBK);
-
-    bool run = wave_active;
-    bool need_mask = kt0 + kBK > Lk;
-    if (CAUSAL && run) {
-      int32_t klo, khi;
-      seg_range(ks, kt0, min(kt0 + kBK, Lk), klo, khi);
-      if (klo > w_qhi) run = false;
-      if (khi > w_qlo) need_mask = true;
-    }
-    if (run) {
-      const bf16x8* Kt = smem[buf][0];
-      const bf16x8* Vt = smem[buf][1];
-      // S^T for two 32-key slices
-      f32x16 s[2];
+  // ---- running state: O^T accumulators (lane: query l32, d 32dt+8i+4h+j)
+  f32x16 o[kQB][DT];
+  float mu[kQB];        // reference value in log2 units of the weights
+  float lpart[kQB][2];  // this lane's share of the row sum, two partial sums
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[st] = f32x16{};
-        const int row = 32 * st + l32;
+  for (int b = 0; b < kQB; ++b) {
 #pragma unroll
-        for (int ksi = 0; ksi < KS; ++ksi) {
-          const bf16x8 kf = Kt[row * CPR + Swz<D>::k(row, 2 * ksi + h)];
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ksi], s[st], 0, 0, 0);
+    for (int t = 0; t < DT; ++t) o[b][t] = f32x16{};
+    mu[b] = kNegInf;
+    lpart[b][0] = lpart[b][1] = 0.f;
+    if (!FUSED && !init && qvalid[b]) {
+      const float* op = Oacc + qbase + (size_t)qrow[b] * D + 4 * h;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 x = *(const f32x4*)(op + 32 * t + 8 * i);
+          o[b][t][4 * i + 0] = x[0];
+          o[b][t][4 * i + 1] = x[1];
+          o[b][t][4 * i + 2] = x[2];
+          o[b][t][4 * i + 3] = x[3];
         }
-      }
-      if (need_mask) {
+      const size_t r = (size_t)prob * Lq + qrow[b];
+      mu[b] = Mst[r] * kLog2e;
+      lpart[b][0] = h == 0 ? Lst[r] : 0.f;
+    }
+  }
+
+  // per-lane LDS read bases within a stage; the rest are immediate offsets.
+  // K (A operand): row 32st+l32, column 2ksi+h.
+  // V^T (transposed reads): row 16kc+4(g>>1)+rr(+8), columns 32t+16(g&1)+4cc..+3
+  // (16-byte column 4t+2(g&1)+(cc>>1), byte 8(cc&1)).
+  const int g = lane >> 4, jj = lane & 15, rr = jj >> 2, cc = jj & 3;
+  const int kread = L::at(l32, h);
+  const int vread = L::TBYTES + L::at(4 * (g >> 1) + rr, 2 * (g & 1) + (cc >> 1)) + 8 * (cc & 1);
+
+  // per-tile facts for this wave
+  struct TileInfo {
+    int32_t kt0;
+    bool mask;       // element mask needed (diagonal, ragged tail, or fully after the queries)
+    bool straddle;   // tile crosses the K segment boundary
+    int32_t kpos0;   // global position of the tile's first row (if not straddling)
+  };
+  auto tile_info = [&](int32_t n) {
+    TileInfo ti;
+    ti.kt0 = tile_kt0(n);
+    const int32_t kend = min(ti.kt0 + kBK, Lk);
+    ti.mask = ti.kt0 + kBK > Lk;
+    ti.straddle = ti.kt0 < ks.len0 && kend > ks.len0;
+    ti.kpos0 = seg_pos(ks, ti.kt0);
+    if (CAUSAL) {
+      int32_t klo, khi;
+      seg_range(ks, ti.kt0, kend, klo, khi);
+      (void)klo;
+      if (khi > w_qlo) ti.mask = true;
+    }
+    return ti;
+  };
+
+  typedef f32x16 Scores[kQB][kNST];  // [query block][32-key part of the tile]
+
+  auto scores = [&](int stage, Scores& s) {
+    const char* kb = smem + stage * L::STAGE + kread;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+    for (int b = 0; b < kQB; ++b)
+#pragma unroll
+      for (int st = 0; st < kNST; ++st) s[b][st] = f32x16{};
+#pragma unroll
+    for (int ksi = 0; ksi < KS; ++ksi)
+#pragma unroll
+      for (int st = 0; st < kNST; ++st) {
+        // rows 32st+l32, column 2ksi+h: the lane base covers l32 and h
+        const bf16x8 kf = lds_b128(kb + L::at(32 * st, 2 * ksi));
+#pragma unroll
+        for (int b = 0; b < kQB; ++b)
+          s[b][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[b][ksi], s[b][st], 0, 0, 0);
+      }
+  };
+
+  auto apply_mask = [&](const TileInfo& ti, Scores& s) {
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      if (!ti.straddle) {
+        // key offset e in the tile is visible iff e <= lim
+        int32_t lim = Lk - 1 - ti.kt0;
+        if (CAUSAL) lim = min(lim, qpos[b] - ti.kpos0);
+#pragma unroll
+        for (int st = 0; st < kNST; ++st)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int32_t kr = kt0 + 32 * st + 8 * i + 4 * h + j;
-              bool masked = kr >= Lk;
-              if (CAUSAL && !masked) masked = seg_pos(ks, kr) > qpos;
-              if (masked) s[st][4 * i + j] = kNegInf;
+              const int e = 32 * st + 8 * i + 4 * h + j;
+              s[b][st][4 * i + j] = e > lim ? kNegInf : s[b][st][4 * i + j];
+            }
+      } else {
+#pragma unroll
+        for (int st = 0; st < kNST; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int32_t kr = ti.kt0 + 32 * st + 8 * i + 4 * h + j;
+              const bool m = kr >= Lk || (CAUSAL && seg_pos(ks, kr) > qpos[b]);
+              s[b][st][4 * i + j] = m ? kNegInf : s[b][st][4 * i + j];
             }
       }
-      // online softmax with lazy rescale
-      float mx = s[0][0];
+    }
+  };
+
+  // row maxima of one tile's scores, log2 units (both lanes of a query agree)
+  auto rowmax = [&](const Scores& s, float (&mt)[kQB]) {
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int b = 0; b < kQB; ++b) {
+      float a[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = partner32_max(mx);
-      const float mt = mx * c_log2;
-      const bool need = mt > mu + kTau;
+      for (int r = 0; r < 8; ++r) {
+        a[r] = fmaxf(s[b][0][2 * r], s[b][0][2 * r + 1]);
+#pragma unroll
+        for (int st = 1; st < kNST; ++st) a[r] = fmaxf(a[r], fmaxf(s[b][st][2 * r], s[b][st][2 * r + 1]));
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = fmaxf(a[r], a[r + 4]);
+      mt[b] = partner32_max(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]))) * c_log2;
+    }
+  };
+
+  // the (rare) rescale of the state when a tile's maximum outgrows the
+  // reference value by more than kTau
+  auto rescale = [&](const float (&mt)[kQB]) {
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      const bool need = mt[b] > mu[b] + kTau;
       if (__builtin_amdgcn_ballot_w64(need)) {
-        // lanes that keep their reference (including rows with no visible key
-        // yet, mu = -inf) must get exactly 1, not exp2(-inf - -inf)
-        const float mnew = need ? mt : mu;
-        const float alpha = need ? fast_exp2(mu - mnew) : 1.f;
-        lrun *= alpha;
+        // lanes keeping their reference (also rows with no visible key yet,
+        // mu = -inf) must get exactly 1, not exp2(-inf - -inf)
+        const float mnew = need ? mt[b] : mu[b];
+        const float alpha = need ? fast_exp2(mu[b] - mnew) : 1.f;
+        lpart[b][0] *= alpha;
+        lpart[b][1] *= alpha;
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-        mu = mnew;
-      }
-      const float mus = mu == kNegInf ? 0.f : mu;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(__builtin_fmaf(s[st][r], c_log2, -mus));
-          lrun += pr;
-          pf[2 * st + r / 8][r % 8] = to_bf16(pr);
-        }
-      // O^T += V^T P^T over four 16-key slices
-      const int g = lane >> 4, jj = lane & 15, rr = jj >> 2, cc = jj & 3;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const int ncol = 32 * t + 16 * (g & 1) + 4 * cc;  // first of 4 columns this lane loads
-          const int ra = 16 * kc + 4 * (g >> 1) + rr;       // key row, first half
-          const int rb = ra + 8;                            // key row, second half
-          const char* base = (const char*)Vt;
-          const char* pa = base + 16 * (ra * CPR + Swz<D>::v(ra, ncol >> 3)) + 2 * (ncol & 7);
-          const char* pb = base + 16 * (rb * CPR + Swz<D>::v(rb, ncol >> 3)) + 2 * (ncol & 7);
-          const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
-          const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pb);
-          const bf16x8 vf = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[t], 0, 0, 0);
-        }
+          for (int r = 0; r < 16; ++r) o[b][t][r] *= alpha;
+        mu[b] = mnew;
       }
     }
-    if (has_next) sstore(buf ^ 1);
+  };
+
+  typedef bf16x8 Probs[kQB][2 * kNST];  // [query block][16-key slice]
+
+  // exponentials of one tile into bf16 B operands (and the row-sum shares)
+  auto exps = [&](const Scores& s, Probs& pf) {
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      const float mus = mu[b] == kNegInf ? 0.f : mu[b];
+#pragma unroll
+      for (int st = 0; st < kNST; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(__builtin_fmaf(s[b][st][r], c_log2, -mus));
+          lpart[b][r & 1] += pr;
+          pf[b][2 * st + r / 8][r % 8] = to_bf16(pr);
+        }
+    }
+  };
+
+#if !RA_STEP_PINGPONG
+  // O^T += V^T P^T for one tile
+  auto pv_tile = [&](int stage, const Probs& pf) {
+    const char* vb = smem + stage * L::STAGE + vread;
+#pragma unroll
+    for (int kc = 0; kc < 2 * kNST; ++kc)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int off = L::at(16 * kc, 4 * t);
+        const bf16x4 va = lds_tr16(vb + off);
+        const bf16x4 vbb = lds_tr16(vb + off + 16 * 8);
+        const bf16x8 vf = {va[0], va[1], va[2], va[3], vbb[0], vbb[1], vbb[2], vbb[3]};
+#pragma unroll
+        for (int b = 0; b < kQB; ++b)
+          o[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[b][kc], o[b][t], 0, 0, 0);
+      }
+  };
+#endif
+
+#if RA_STEP_PINGPONG
+  // The matrix phase of one tile in a fixed order: the score MFMAs of the next
+  // tile, then the PV MFMAs of this one. Each step's LDS operand is read
+  // kAhead steps earlier and scheduling barriers keep that order, so no MFMA
+  // waits on a just-issued LDS read.
+  Scores sc;
+  Probs pf;
+  auto mfma_phase = [&](int kstage, int vstage) {
+    constexpr int kAhead = RA_STEP_LDS_AHEAD;
+    constexpr int NSC = KS * kNST;      // score steps
+    constexpr int NPV = 2 * kNST * DT;  // PV steps
+    const char* kb = smem + kstage * L::STAGE + kread;
+    const char* vb = smem + vstage * L::STAGE + vread;
+#pragma unroll
+    for (int b = 0; b < kQB; ++b)
+#pragma unroll
+      for (int st = 0; st < kNST; ++st) sc[b][st] = f32x16{};
+    auto operand = [&](int i) -> bf16x8 {
+      if (i < NSC) return lds_b128(kb + L::at(32 * (i % kNST), 2 * (i / kNST)));
+      const int j = i - NSC, off = L::at(16 * (j / DT), 4 * (j % DT));
+      const bf16x4 va = lds_tr16(vb + off);
+      const bf16x4 vbb = lds_tr16(vb + off + 16 * 8);
+      return bf16x8{va[0], va[1], va[2], va[3], vbb[0], vbb[1], vbb[2], vbb[3]};
+    };
+    bf16x8 op[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) op[j] = operand(j);
+#pragma unroll
+    for (int i = 0; i < NSC + NPV; ++i) {
+      const bf16x8 cur = op[i % kAhead];
+      if (i < NSC) {
+        const int st = i % kNST, ksi = i / kNST;
+#pragma unroll
+        for (int b = 0; b < kQB; ++b)
+          sc[b][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[b][ksi], sc[b][st], 0, 0, 0);
+      } else {
+        const int j = i - NSC, kc = j / DT, t = j % DT;
+#pragma unroll
+        for (int b = 0; b < kQB; ++b)
+          o[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[b][kc], o[b][t], 0, 0, 0);
+      }
+      if (i + kAhead < NSC + NPV) op[i % kAhead] = operand(i + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- ping-pong schedule. The two halves of the workgroup (waves 0..W/2-1
+  // and W/2..W-1, one of each on every SIMD) run the same per-tile program
+  // shifted by half an iteration: while one wave of a SIMD issues its matrix
+  // work (scores of tile n+1 and PV of tile n), the other does its vector
+  // work (mask, row maximum, rescale and exponentials of its next tile), so
+  // the matrix core always has a wave feeding it. Time advances in slots that
+  // end with a workgroup barrier:
+  //   group A: slot 0 = start (scores + softmax of tile 0), then slot 2n+1 =
+  //            matrix phase n, slot 2n+2 = vector phase n;
+  //   group B: the same, one slot later.
+  // The matrix phase n reads K of tile n+1 and V of tile n, so tile m is
+  // needed from slot 2m-1 and free after slot 2m+2: tile m+kStages is
+  // requested at the start of slot 2m+3 into m's stage, and tile n+1 is
+  // waited for at the end of slot 2n.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // group B; the SIMD a wave lands on follows its index modulo 4 or pairs of
+  // consecutive waves share one, so both choices of split are measured
+#if RA_STEP_GROUP_ODD
+  const bool late = (w & 1) != 0;
+#else
+  const bool late = w >= kWaves / 2;
+#endif
+  auto vector_phase = [&](int32_t n) {  // softmax of tile n (scores in sc)
+    const TileInfo ti = tile_info(n);
+    if (ti.mask) apply_mask(ti, sc);
+    float mt[kQB];
+    rowmax(sc, mt);
+    rescale(mt);
+    exps(sc, pf);
+  };
+  const int32_t nslots = ntiles > 0 ? 2 * ntiles + 1 : 0;
+  for (int32_t s = 0; s < nslots; ++s) {
+    if ((s & 1) && s >= 3) {
+      const int32_t m = (s - 3) >> 1;
+      if (m + kStages < ntiles) fetch(m + kStages, m % kStages);
+    }
+    const int32_t a = late ? s - 1 : s;  // this group's own slot number
+    if (a == 0) {
+      scores(0, sc);
+      vector_phase(0);
+    } else if (a > 0 && (a & 1)) {
+      const int32_t n = (a - 1) >> 1;
+      if (n < ntiles) {
+        __builtin_amdgcn_s_setprio(1);
+        // past the last tile the scores read a stale stage and are never used
+        mfma_phase((n + 1) % kStages, n % kStages);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    } else if (a > 0) {
+      const int32_t n = (a - 2) >> 1;
+      if (n + 1 < ntiles) vector_phase(n + 1);
+    }
+    if (!(s & 1)) {
+      // end of slot 2n: tile n+1 must be in LDS; tiles requested later may
+      // stay in flight
+      const int32_t n = s >> 1;
+      const int32_t latest = min(ntiles - 1, n + kStages - 2);  // requested so far
+      const int32_t in_flight = latest - (n + 1);
+      if (in_flight >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA));
+      else if (in_flight == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
     __syncthreads();
   }
 
+#else
+  // ---- prologue: every load issued so far (first tiles, Q, state) must have
+  // landed. Waiting for all of them also leaves no compiler-tracked load
+  // pending, so no wait inside the loop is tied to the prologue.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // One pipelined iteration over tile n (scores `cur`, row max `mcur` known):
+  //   request tile n+kStages-1 into the stage tile n-1 used;
+  //   rescale the state if tile n's maximum demands it;
+  //   the score MFMAs of tile n+1 (into `nxt`) with the exponentials of tile
+  //   n, then the PV MFMAs of tile n with the row maximum of tile n+1;
+  //   the rare masked tiles get their mask and maximum redone afterwards;
+  //   wait for tile n+2's loads; one barrier.
+  // Past the last tile the score MFMAs read a stale stage and their result is
+  // never used.
+  int stage = 0;  // LDS stage of tile n
+  auto body = [&](int32_t n, Scores& cur, float (&mcur)[kQB], Scores& nxt, float (&mnxt)[kQB]) {
+    const int stage1 = stage + 1 == kStages ? 0 : stage + 1;
+    const int32_t nf = n + kStages - 1;  // tile requested in this iteration
+    if (nf < ntiles) fetch(nf, stage == 0 ? kStages - 1 : stage - 1);
+    rescale(mcur);
+    Probs pf;
+    scores(stage1, nxt);
+    exps(cur, pf);
+    pv_tile(stage, pf);
+    rowmax(nxt, mnxt);
+    if (n + 1 < ntiles) {
+      const TileInfo ti = tile_info(n + 1);
+      if (ti.mask) {
+        apply_mask(ti, nxt);
+        rowmax(nxt, mnxt);
+      }
+    }
+    // tile n+2 must be in LDS before the barrier; the later ones (requested
+    // in this and the previous kStages-4 iterations) may stay in flight
+    const int32_t in_flight = min(ntiles - 1, nf) - (n + 2);
+    if (in_flight >= kStages - 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 3) * NDMA));
+    else if (in_flight == 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA));
+    else if (in_flight == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    stage = stage1;
+  };
+
+  Scores sa, sb;
+  float ma[kQB], mb[kQB];
+  if (ntiles > 0) {
+    scores(0, sa);
+    const TileInfo ti = tile_info(0);
+    if (ti.mask) apply_mask(ti, sa);
+    rowmax(sa, ma);
+  }
+  for (int32_t n = 0; n < ntiles; n += 2) {
+    body(n, sa, ma, sb, mb);
+    if (n + 1 < ntiles) body(n + 1, sb, mb, sa, ma);
+  }
+
+#endif
+
   if (!wave_active) return;
-  const float lsum = partner32_sum(lrun);
-  if (FUSED) {
-    if (!qvalid) return;
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    bf16* op = Out + qbase + (size_t)qrow * D + 4 * h;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+  for (int b = 0; b < kQB; ++b) {
+    const float lsum = partner32_sum(lpart[b][0] + lpart[b][1]);
+    if (!qvalid[b]) continue;
+    if (FUSED) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      bf16* op = Out + qbase + (size_t)qrow[b] * D + 4 * h;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4 y = {to_bf16(o[t][4 * i + 0] * inv), to_bf16(o[t][4 * i + 1] * inv),
-                    to_bf16(o[t][4 * i + 2] * inv), to_bf16(o[t][4 * i + 3] * inv)};
-        *(bf16x4*)(op + 32 * t + 8 * i) = y;
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x4 y = {to_bf16(o[b][t][4 * i + 0] * inv), to_bf16(o[b][t][4 * i + 1] * inv),
+                      to_bf16(o[b][t][4 * i + 2] * inv), to_bf16(o[b][t][4 * i + 3] * inv)};
+          *(bf16x4*)(op + 32 * t + 8 * i) = y;
+        }
+      if (Lse && h == 0)
+        Lse[(size_t)prob * Lq + qrow[b]] = lsum > 0.f ? (mu[b] + fast_log2(lsum)) * kLn2 : kNegInf;
+    } else {
+      float* op = Oacc + qbase + (size_t)qrow[b] * D + 4 * h;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 y = {o[b][t][4 * i + 0], o[b][t][4 * i + 1], o[b][t][4 * i + 2], o[b][t][4 * i + 3]};
+          *(f32x4*)(op + 32 * t + 8 * i) = y;
+        }
+      if (h == 0) {
+        const size_t r = (size_t)prob * Lq + qrow[b];
+        Mst[r] = mu[b] * kLn2;
+        Lst[r] = lsum;
       }
-    if (Lse && h == 0)
-      Lse[(size_t)prob * Lq + qrow] = lsum > 0.f ? (mu + fast_log2(lsum)) * kLn2 : kNegInf;
-  } else {
-    if (!qvalid) return;
-    float* op = Oacc + qbase + (size_t)qrow * D + 4 * h;
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 y = {o[t][4 * i + 0], o[t][4 * i + 1], o[t][4 * i + 2], o[t][4 * i + 3]};
-        *(f32x4*)(op + 32 * t + 8 * i) = y;
-      }
-    if (h == 0) {
-      const size_t r = (size_t)prob * Lq + qrow;
-      Mst[r] = mu * kLn2;
-      Lst[r] = lsum;
     }
   }
 }
