@@ -66,6 +66,14 @@ def ring_flop(w, rank, segs):
     return [sizing.attention_flop(p, w.d, w.B * w.H) for p in per_step]
 
 
+# Sources that define the ring-step kernel; a change to any of them makes the
+# committed HBM counter figures stale (traffic is then reported as null).
+STEP_SOURCES = {
+    torch.bfloat16: ["step_mfma.hip", "ra_device.h", "ra_launch.h"],
+    torch.float32: ["step_f32.hip", "ra_device.h", "ra_launch.h"],
+}
+
+
 def kernel_source_hash(names):
     h = hashlib.sha256()
     for n in names:
@@ -131,10 +139,11 @@ def legs(w, q, dev, reps):
     out = {}
     # LSE merge of two normalised partials of this workload's shape (bf16)
     B, H, L, d = q.shape
-    oa = torch.randn_like(q)
-    ob = torch.randn_like(q)
-    la = torch.randn((B, H, L), device=dev)
-    lb = torch.randn((B, H, L), device=dev)
+    g = torch.Generator(device=dev).manual_seed(20261)
+    oa = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+    ob = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+    la = torch.randn((B, H, L), generator=g, device=dev)
+    lb = torch.randn((B, H, L), generator=g, device=dev)
     oo, lo = torch.empty_like(q), torch.empty_like(la)
     ms = time_kernel(lambda: _lib.ra_merge_lse(oa, la, ob, lb, oo, lo), reps)
     nbytes = 3 * q.numel() * q.element_size() + 3 * la.numel() * 4
@@ -251,7 +260,7 @@ def main():
     value = total * args.steps / wall / 1e12
     k_mean_ms = float(kms.mean())
     achieved = (total / w.P) / (k_mean_ms * 1e-3)
-    src_hash = kernel_source_hash(["step_mfma.hip"] if w.dtype == torch.bfloat16 else ["step_f32.hip"])
+    src_hash = kernel_source_hash(STEP_SOURCES[w.dtype])
     traffic = load_traffic("ra_step:" + w.name, src_hash)
     rec = {
         "metric": "attention TFLOP/s per MI355X (and % bf16 MFMA peak), ring-step kernel",
