@@ -53,10 +53,24 @@ __device__ __forceinline__ void seg_range(const DevSegs& s, int32_t r0, int32_t 
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 __device__ __forceinline__ float from_bf16(bf16 x) { return (float)x; }
 
+// Maxima of values that are never NaN (scores of finite inputs, or -inf):
+// single v_max / v_max3 instructions. fmaxf would first quiet possible
+// signalling NaNs of every operand, doubling the instruction count.
+__device__ __forceinline__ float max2_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_nn(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Value of `x` held by lane (lane ^ 32), via the gfx950 32-lane swap.
 __device__ __forceinline__ float partner32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float partner32_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -185,6 +185,37 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   const int32_t ntiles = n0 + n1;
   auto tile_kt0 = [&](int32_t n) { return (n < n0 ? t0a + n : t1a + (n - n0)) * kBK; };
 
+  // ---- a query tile that sees no key of this block keeps its state: no
+  // loads and no stores, except that a first step stores the empty state
+  // (and a fused call the empty output: zeros, lse -inf)
+  if (ntiles == 0) {
+    if ((!FUSED && !init) || !wave_active) return;
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      if (!qvalid[b]) continue;
+      const size_t r = (size_t)prob * Lq + qrow[b];
+      if (FUSED) {
+        bf16* op = Out + qbase + (size_t)qrow[b] * D + 4 * h;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *(bf16x4*)(op + 32 * t + 8 * i) = bf16x4{};
+        if (Lse && h == 0) Lse[r] = kNegInf;
+      } else {
+        float* op = Oacc + qbase + (size_t)qrow[b] * D + 4 * h;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *(f32x4*)(op + 32 * t + 8 * i) = f32x4{};
+        if (h == 0) {
+          Mst[r] = kNegInf;
+          Lst[r] = 0.f;
+        }
+      }
+    }
+    return;
+  }
+
   // ---- K/V tiles: bounds-checked buffer loads straight into LDS. Load run r
   // of a tile holds columns r, r+NRUN, ... of rows 0..kBK-1; lane i brings
   // row i % kBK of column r + NRUN * (i / kBK). A wave owns RUNS_PER_WAVE runs.
@@ -333,16 +364,19 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   auto rowmax = [&](const Scores& s, float (&mt)[kQB]) {
 #pragma unroll
     for (int b = 0; b < kQB; ++b) {
-      float a[8];
+      // 16*kNST values: chains of v_max3, two values per instruction
+      float a[4];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        a[r] = fmaxf(s[b][0][2 * r], s[b][0][2 * r + 1]);
+      for (int c = 0; c < 4; ++c) {
+        a[c] = max2_nn(s[b][0][4 * c], s[b][0][4 * c + 1]);
+        a[c] = max3_nn(a[c], s[b][0][4 * c + 2], s[b][0][4 * c + 3]);
 #pragma unroll
-        for (int st = 1; st < kNST; ++st) a[r] = fmaxf(a[r], fmaxf(s[b][st][2 * r], s[b][st][2 * r + 1]));
+        for (int st = 1; st < kNST; ++st) {
+          a[c] = max3_nn(a[c], s[b][st][4 * c], s[b][st][4 * c + 1]);
+          a[c] = max3_nn(a[c], s[b][st][4 * c + 2], s[b][st][4 * c + 3]);
+        }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = fmaxf(a[r], a[r + 4]);
-      mt[b] = partner32_max(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]))) * c_log2;
+      mt[b] = partner32_max(max3_nn(max2_nn(a[0], a[1]), a[2], a[3])) * c_log2;
     }
   };
 
@@ -370,7 +404,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
 
   typedef bf16x8 Probs[kQB][2 * kNST];  // [query block][16-key slice]
 
-  // exponentials of one tile into bf16 B operands (and the row-sum shares)
+  // exponentials of one tile into bf16 B operands (and the row-sum shares,
+  // summed in fp32 before rounding so that lse keeps full precision)
   auto exps = [&](const Scores& s, Probs& pf) {
 #pragma unroll
     for (int b = 0; b < kQB; ++b) {
@@ -385,6 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
         }
     }
   };
+
 
 #if !RA_STEP_PINGPONG
   // O^T += V^T P^T for one tile

@@ -194,6 +194,22 @@ def test_rows_without_visible_keys(gpu_lib):
     assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
 
 
+def test_block_after_every_query_leaves_state_untouched(gpu_lib):
+    banner("causal step whose block lies after every local query: state bitwise unchanged")
+    d, B, H, L = 128, 1, 3, 700
+    q = seeded.gen_bhsd(82, 0, B, H, 0, L, d, torch.bfloat16, "cuda")
+    k = seeded.gen_bhsd(82, 1, B, H, 0, L, d, torch.bfloat16, "cuda")
+    v = seeded.gen_bhsd(82, 2, B, H, 0, L, d, torch.bfloat16, "cuda")
+    st = ring.RingState(B, H, L, d, "cuda")
+    _lib.ra_step(q, k, v, [(0, L)], [(0, L)], True, d ** -0.5, st.o, st.m, st.l, init=True)
+    before = (st.o.clone(), st.m.clone(), st.l.clone())
+    # the second block starts after the last query: no query tile sees any key
+    _lib.ra_step(q, k, v, [(0, L)], [(L, L)], True, d ** -0.5, st.o, st.m, st.l)
+    torch.cuda.synchronize()
+    for a, b in zip(before, (st.o, st.m, st.l)):
+        assert torch.equal(a, b)
+
+
 # ---- invariants on the GPU --------------------------------------------------------
 
 @pytest.fixture(scope="module")
