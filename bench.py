@@ -159,8 +159,11 @@ def legs(w, q, dev, reps):
     fl = sizing.attention_flop(v.T * v.S_sp * v.S_sp, v.d, v.B * v.H)
     out["factored_spatial"] = {"workload": v.name, "ms": ms, "TFLOP/s": fl / ms / 1e9,
                                "mfma_frac": fl / ms / 1e-3 / PEAK_BF16_DENSE}
-    # temporal: flush caches between reps by touching a 1 GiB buffer
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    # temporal: evict the inputs from L2 and the last-level cache between reps
+    # by reading a 1 GiB buffer (a read leaves clean lines behind, so no
+    # write-back of the flush data lands inside the timed kernel)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def temporal():
         _lib.ra_factored_temporal(qv, kvv, vv, v.T, v.S_sp, v.scale, ov, lv)
@@ -168,7 +171,7 @@ def legs(w, q, dev, reps):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     tms = []
     for i in range(reps + 2):
-        flush.fill_(float(i))
+        torch.sum(flush, dim=0, out=sink)
         e0.record()
         temporal()
         e1.record()
@@ -179,7 +182,7 @@ def legs(w, q, dev, reps):
     nbytes = 4 * qv.numel() * qv.element_size() + lv.numel() * 4
     out["factored_temporal"] = {"workload": v.name, "ms": ms, "GB/s": nbytes / ms / 1e6,
                                 "hbm_frac": nbytes / ms / 1e-3 / PEAK_HBM,
-                                "algorithmic_bytes": nbytes, "caches": "flushed (1 GiB write) before each rep"}
+                                "algorithmic_bytes": nbytes, "caches": "evicted by reading 1 GiB before each rep"}
     return out
 
 
@@ -228,6 +231,8 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-prefetch", action="store_true", help="pass each block on the compute stream")
     ap.add_argument("--no-legs", action="store_true")
+    ap.add_argument("--legs-only", action="store_true",
+                    help="time only the merge / factored legs (for profiling those kernels) and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -253,6 +258,10 @@ def main():
         return
 
     w = configs.RING_WORKLOADS[args.workload]
+    if args.legs_only:
+        q = torch.empty((w.B, w.H, w.L, w.d), dtype=w.dtype, device=dev)
+        print(json.dumps({"legs": legs(w, q, dev, reps=args.steps)}), flush=True)
+        return
     log(f"[bench] workload {w.name} rank {args.rank}: generating inputs")
     q, segs, kv = make_ring_inputs(w, args.rank, dev)
     flops = ring_flop(w, args.rank, segs)

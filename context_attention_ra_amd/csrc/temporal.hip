@@ -54,14 +54,36 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(
   const size_t base = (size_t)prob * N * D;
   auto row_off = [&](int t) { return base + ((size_t)t * S_sp + s) * D; };
 
-  // V rows -> LDS (swizzled), zero for frames t >= T
+  // Every global load is issued before any result is used, so a wave waits
+  // for memory once. Rows of frames t >= T are clamped to a valid row and
+  // zeroed after the load.
+  constexpr int NV = kT * CPR / 64;  // 16-byte V chunks per lane
+  u32x4 vx[NV];
 #pragma unroll
-  for (int i = 0; i < kT * CPR / 64; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int id = lane + 64 * i;
     const int t = id / CPR, c = id % CPR;
-    u32x4 x = {0, 0, 0, 0};
-    if (t < T) x = *(const u32x4*)(V + row_off(t) + 8 * c);
-    *(u32x4*)&vs[w][t * CPR + tswz<D>(t, c)] = x;
+    vx[i] = *(const u32x4*)(V + row_off(t < T ? t : T - 1) + 8 * c);
+  }
+  // scores: S^T[t'][t] with A = K (row t' = lane%16), B = Q^T (column t = lane%16)
+  const int t16 = lane & 15, g = lane >> 4;
+  const bool ok = t16 < T;
+  bf16x8 kf[KS], qf[KS];
+  {
+    const bf16* kp = K + row_off(ok ? t16 : 0) + 8 * g;
+    const bf16* qp = Q + row_off(ok ? t16 : 0) + 8 * g;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      kf[k] = *(const bf16x8*)(kp + 32 * k);
+      qf[k] = *(const bf16x8*)(qp + 32 * k);
+    }
+  }
+  // V rows -> LDS (swizzled), zero for frames t >= T
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int id = lane + 64 * i;
+    const int t = id / CPR, c = id % CPR;
+    *(u32x4*)&vs[w][t * CPR + tswz<D>(t, c)] = t < T ? vx[i] : u32x4{0, 0, 0, 0};
   }
   // the slot is private to this wave: a wave-scope fence orders the writes
   // above before the transposed reads below
@@ -69,29 +91,16 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // scores: S^T[t'][t] with A = K (row t' = lane%16), B = Q^T (column t = lane%16)
-  const int t16 = lane & 15, g = lane >> 4;
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-  {
-    const bool ok = t16 < T;
-    const bf16* kp = K + row_off(ok ? t16 : 0) + 8 * g;
-    const bf16* qp = Q + row_off(ok ? t16 : 0) + 8 * g;
-    bf16x8 kf[KS], qf[KS];
+  if (!ok) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      kf[k] = *(const bf16x8*)(kp + 32 * k);
-      qf[k] = *(const bf16x8*)(qp + 32 * k);
+      kf[k] = bf16x8{};
+      qf[k] = bf16x8{};
     }
-    if (!ok) {
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        kf[k] = bf16x8{};
-        qf[k] = bf16x8{};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < KS; ++k) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], sc, 0, 0, 0);
   }
+#pragma unroll
+  for (int k = 0; k < KS; ++k) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], sc, 0, 0, 0);
   // lane holds keys t' = 4g + j of query t16
   float x[4];
 #pragma unroll
