@@ -14,7 +14,8 @@
 //   keys of one query, and the row max / row sum finish with two lane swaps.
 // * Probabilities are normalised in registers and used as the B operand of
 //   O^T = V^T P^T (v_mfma_f32_16x16x16_bf16); V goes through a 4 KiB
-//   per-wave LDS slot so its transpose comes from ds_read_b64_tr_b16.
+//   per-wave LDS slot so its transpose comes from ds_read_b64_tr_b16, and the
+//   output goes back out through the same slot as whole rows.
 // * Frames t >= T (when T < 16) are zero-filled and masked.
 
 #include "ra_device.h"
@@ -124,7 +125,11 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(
   const int rr = t16 >> 2, cc = t16 & 3;
   const int vrow = 4 * g + rr;
   const bool store = t16 < T;
-  bf16* op = Out + row_off(store ? t16 : 0) + 4 * g;
+  // The output goes out through the wave's LDS slot, so that each store
+  // instruction writes four whole rows instead of 32-byte pieces of sixteen.
+  // Lane (t16, g) holds dims 16dt+4g..+3 of frame t16; it overwrites V
+  // columns that only this iteration reads, after its reads (a wave's LDS
+  // operations run in order).
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const int ncol = 16 * dt + 4 * cc;
@@ -132,10 +137,18 @@ __global__ __launch_bounds__(kThreads) void temporal_kernel(
     const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)pa);
     const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
         __builtin_bit_cast(s16x4, va), pf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    if (store) {
-      bf16x4 y = {to_bf16(acc[0]), to_bf16(acc[1]), to_bf16(acc[2]), to_bf16(acc[3])};
-      *(bf16x4*)(op + 16 * dt) = y;
-    }
+    *(bf16x4*)((char*)vs[w] + 16 * (t16 * CPR + tswz<D>(t16, 2 * dt + (g >> 1))) + 8 * (g & 1)) =
+        bf16x4{to_bf16(acc[0]), to_bf16(acc[1]), to_bf16(acc[2]), to_bf16(acc[3])};
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int id = lane + 64 * i;
+    const int t = id / CPR, c = id % CPR;
+    const u32x4 x = *(const u32x4*)&vs[w][t * CPR + tswz<D>(t, c)];
+    if (t < T) *(u32x4*)(Out + row_off(t) + 8 * c) = x;
   }
   if (Lse && g == 0 && store) Lse[(size_t)prob * N + (size_t)t16 * S_sp + s] = (mx + fast_log2(sum)) * kLn2;
 }
