@@ -171,6 +171,9 @@ ra_status ra_factored_spatial(const void* q, const void* k, const void* v, ra_dt
                               void* out, float* lse, hipStream_t stream) {
   const ra_status st = factored_check(q, k, v, dt, B, H, T, S_sp, d, scale, out, lse);
   if (st != RA_OK) return st;
+  // one frame of K or V must be addressable by a 32-bit offset
+  if ((int64_t)S_sp * d * (int64_t)esize(dt) > (int64_t)INT32_MAX) return RA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * T * ((S_sp + 255) / 256) > (int64_t)INT32_MAX / 2) return RA_ERR_UNSUPPORTED;
   // every frame is an independent unmasked S_sp x S_sp problem: rows of frame t
   // of slice (b, h) are contiguous, so the frames are simply B*H*T slices
   return hip_fail(ra::launch_attend_bf16(q, k, v, B * H * T, S_sp, d, scale, out, lse, stream));

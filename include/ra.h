@@ -150,7 +150,8 @@ ra_status ra_merge_lse(const void* o_a, const float* lse_a,
  * Under a temporal-first split this is fully local to a device.
  * Errors: RA_ERR_INVALID_ARG for null required pointers, sizes <= 0,
  *   T*S_sp > INT32_MAX, bad scale or out/lse overlapping inputs;
- *   RA_ERR_UNSUPPORTED for dt != RA_BF16 or d not in {64, 128}.
+ *   RA_ERR_UNSUPPORTED for dt != RA_BF16, d not in {64, 128}, or one frame
+ *   of K/V larger than INT32_MAX bytes.
  */
 ra_status ra_factored_spatial(const void* q, const void* k, const void* v, ra_dtype dt,
                               int32_t B, int32_t H, int32_t T, int32_t S_sp, int32_t d,
@@ -160,7 +161,8 @@ ra_status ra_factored_spatial(const void* q, const void* k, const void* v, ra_dt
  * ra_factored_temporal — temporal half of factored video attention (same
  * section): each query at (t, s) attends without a mask to the T keys
  * {t'*S_sp + s : t' < T} at its spatial position. T must be 1..16.
- * Arguments and errors as ra_factored_spatial; T > 16 is RA_ERR_UNSUPPORTED.
+ * Arguments and errors as ra_factored_spatial (without the per-frame size
+ * limit); T > 16 is RA_ERR_UNSUPPORTED.
  */
 ra_status ra_factored_temporal(const void* q, const void* k, const void* v, ra_dtype dt,
                                int32_t B, int32_t H, int32_t T, int32_t S_sp, int32_t d,

@@ -120,6 +120,9 @@ def test_factored_validation(lib):
         assert fn(ptr(0), ptr(1), ptr(2), 1, 1, 1, 4, 9, 32, 0.1, ptr(3), None, None) == UNS
     assert lib.ra_factored_temporal(ptr(0), ptr(1), ptr(2), 1, 1, 1, 17, 9, 128, 0.1, ptr(3),
                                     None, None) == UNS
+    # offsets inside one frame of the spatial kernel are 32-bit
+    assert lib.ra_factored_spatial(ptr(0), ptr(1), ptr(2), 1, 1, 1, 1, 1 << 23, 128, 0.1, ptr(3),
+                                   None, None) == UNS
 
 
 def test_kv_pass_validation(lib):
