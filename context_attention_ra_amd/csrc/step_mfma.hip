@@ -9,17 +9,14 @@
 // the k8ai page needs no special casing here.
 //
 // Design (CDNA4-first; FlashAttention is prior art, not the template):
-// * A workgroup is kWaves waves and each wave owns 32*kQB query rows. With
-//   two 32-row blocks per wave every K or V fragment a wave reads from LDS
-//   feeds two MFMAs, which halves LDS traffic per FLOP: on gfx950 the
-//   transposed LDS read runs at about half the rate of a plain 16-byte read
-//   and would otherwise rival the matrix-core time.
+// * A workgroup is eight waves of 32 query rows (256 rows). Each K or V
+//   fragment a wave reads from LDS feeds one MFMA; on gfx950 the transposed
+//   LDS read of V runs at about half the rate of a plain 16-byte read.
 // * Keys stream through a kStages-deep LDS ring in tiles of kBK rows, fetched
 //   by bounds-checked buffer loads that write LDS directly (no staging
-//   registers; rows past the block read as zero). A tile is requested
-//   kStages-1 iterations before it is consumed and waited for only just
-//   before, so global latency hides behind several iterations; one barrier
-//   per tile.
+//   registers; rows past the block read as zero). A tile is requested about
+//   three slots before it is consumed and waited for only just before, so
+//   global latency hides behind several slots.
 // * LDS holds each tile column-major in 16-byte columns; one load instruction
 //   fills a 1 KiB run (one or two columns), runs padded to 1088 bytes. Both the
 //   16-byte K reads and the transposed V reads are then free of bank
@@ -28,9 +25,11 @@
 //   the 32x32 accumulator layout gives every lane one query column and 16 of
 //   each 32 keys, so a row maximum is an in-lane reduction plus one 32-lane
 //   swap (v_permlane32_swap), and the per-query rescale factor is a lane scalar.
-// * Software pipelining inside each wave: the score MFMAs of tile n+1 are
-//   issued next to the exponentials of tile n, and the PV MFMAs of tile n next
-//   to the row maximum of tile n+1, so matrix core and vector ALUs overlap.
+// * Ping-pong: the two halves of the workgroup (one wave of each on every
+//   SIMD) alternate, one slot apart, between a matrix phase (scores of tile
+//   n+1 and PV of tile n) and a vector phase (mask, row maximum, rescale and
+//   exponentials), so one wave feeds the matrix core while the other computes
+//   exponentials; a workgroup barrier ends every slot.
 // * The probabilities stay in registers as the B operand of O^T += V^T P^T.
 //   The key order inside each 16-key MFMA slice is permuted to match the
 //   accumulator layout; the matching V^T operand is read with the gfx950
@@ -48,35 +47,14 @@
 #include "ra_device.h"
 #include "ra_launch.h"
 
-#ifndef RA_STEP_WAVES
-#define RA_STEP_WAVES 8
-#endif
-#ifndef RA_STEP_QBLOCKS
-#define RA_STEP_QBLOCKS 1
-#endif
-#ifndef RA_STEP_BK
-#define RA_STEP_BK 64
-#endif
-#ifndef RA_STEP_STAGES
-#define RA_STEP_STAGES 4
-#endif
-#ifndef RA_STEP_PINGPONG
-#define RA_STEP_PINGPONG 1
-#endif
-#ifndef RA_STEP_GROUP_ODD
-#define RA_STEP_GROUP_ODD 0
-#endif
-#ifndef RA_STEP_LDS_AHEAD
-#define RA_STEP_LDS_AHEAD 3
-#endif
-
 namespace ra {
 namespace {
 
-constexpr int kWaves = RA_STEP_WAVES;   // waves per workgroup
-constexpr int kQB = RA_STEP_QBLOCKS;    // 32-row query blocks per wave
-constexpr int kBK = RA_STEP_BK;         // key rows per tile (32 or 64)
-constexpr int kStages = RA_STEP_STAGES; // LDS ring depth
+constexpr int kWaves = 8;               // waves per workgroup
+constexpr int kQB = 1;                  // 32-row query blocks per wave
+constexpr int kBK = 64;                 // key rows per tile (32 or 64)
+constexpr int kStages = 4;              // LDS ring depth
+constexpr int kAhead = 3;               // LDS operands read ahead of their MFMA
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBQ = 32 * kQB * kWaves;  // query rows per workgroup
 constexpr int kNST = kBK / 32;          // 32-key halves per tile
@@ -236,9 +214,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   };
 
   // the first tiles are requested before the Q and state loads
-  constexpr int kPrologueTiles = RA_STEP_PINGPONG ? kStages : kStages - 1;
 #pragma unroll
-  for (int i = 0; i < kPrologueTiles; ++i)
+  for (int i = 0; i < kStages; ++i)
     if (ntiles > i) fetch(i, i);
 
   // ---- query fragments: B operand of S^T = K Q^T (lane: query l32, d 16ks+8h..+8)
@@ -422,26 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   };
 
 
-#if !RA_STEP_PINGPONG
-  // O^T += V^T P^T for one tile
-  auto pv_tile = [&](int stage, const Probs& pf) {
-    const char* vb = smem + stage * L::STAGE + vread;
-#pragma unroll
-    for (int kc = 0; kc < 2 * kNST; ++kc)
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const int off = L::at(16 * kc, 4 * t);
-        const bf16x4 va = lds_tr16(vb + off);
-        const bf16x4 vbb = lds_tr16(vb + off + 16 * 8);
-        const bf16x8 vf = {va[0], va[1], va[2], va[3], vbb[0], vbb[1], vbb[2], vbb[3]};
-#pragma unroll
-        for (int b = 0; b < kQB; ++b)
-          o[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[b][kc], o[b][t], 0, 0, 0);
-      }
-  };
-#endif
 
-#if RA_STEP_PINGPONG
   // The matrix phase of one tile in a fixed order: the score MFMAs of the next
   // tile, then the PV MFMAs of this one. Each step's LDS operand is read
   // kAhead steps earlier and scheduling barriers keep that order, so no MFMA
@@ -449,7 +407,6 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   Scores sc;
   Probs pf;
   auto mfma_phase = [&](int kstage, int vstage) {
-    constexpr int kAhead = RA_STEP_LDS_AHEAD;
     constexpr int NSC = KS * kNST;      // score steps
     constexpr int NPV = 2 * kNST * DT;  // PV steps
     const char* kb = smem + kstage * L::STAGE + kread;
@@ -504,13 +461,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // group B; the SIMD a wave lands on follows its index modulo 4 or pairs of
-  // consecutive waves share one, so both choices of split are measured
-#if RA_STEP_GROUP_ODD
-  const bool late = (w & 1) != 0;
-#else
+  // group B: waves w and w + 4 share a SIMD
   const bool late = w >= kWaves / 2;
-#endif
   auto vector_phase = [&](int32_t n) {  // softmax of tile n (scores in sc)
     const TileInfo ti = tile_info(n);
     if (ti.mask) apply_mask(ti, sc);
@@ -557,69 +509,6 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     __syncthreads();
   }
 
-#else
-  // ---- prologue: every load issued so far (first tiles, Q, state) must have
-  // landed. Waiting for all of them also leaves no compiler-tracked load
-  // pending, so no wait inside the loop is tied to the prologue.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
-
-  // One pipelined iteration over tile n (scores `cur`, row max `mcur` known):
-  //   request tile n+kStages-1 into the stage tile n-1 used;
-  //   rescale the state if tile n's maximum demands it;
-  //   the score MFMAs of tile n+1 (into `nxt`) with the exponentials of tile
-  //   n, then the PV MFMAs of tile n with the row maximum of tile n+1;
-  //   the rare masked tiles get their mask and maximum redone afterwards;
-  //   wait for tile n+2's loads; one barrier.
-  // Past the last tile the score MFMAs read a stale stage and their result is
-  // never used.
-  int stage = 0;  // LDS stage of tile n
-  auto body = [&](int32_t n, Scores& cur, float (&mcur)[kQB], Scores& nxt, float (&mnxt)[kQB]) {
-    const int stage1 = stage + 1 == kStages ? 0 : stage + 1;
-    const int32_t nf = n + kStages - 1;  // tile requested in this iteration
-    if (nf < ntiles) fetch(nf, stage == 0 ? kStages - 1 : stage - 1);
-    rescale(mcur);
-    Probs pf;
-    scores(stage1, nxt);
-    exps(cur, pf);
-    pv_tile(stage, pf);
-    rowmax(nxt, mnxt);
-    if (n + 1 < ntiles) {
-      const TileInfo ti = tile_info(n + 1);
-      if (ti.mask) {
-        apply_mask(ti, nxt);
-        rowmax(nxt, mnxt);
-      }
-    }
-    // tile n+2 must be in LDS before the barrier; the later ones (requested
-    // in this and the previous kStages-4 iterations) may stay in flight
-    const int32_t in_flight = min(ntiles - 1, nf) - (n + 2);
-    if (in_flight >= kStages - 3)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 3) * NDMA));
-    else if (in_flight == 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA));
-    else if (in_flight == 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    stage = stage1;
-  };
-
-  Scores sa, sb;
-  float ma[kQB], mb[kQB];
-  if (ntiles > 0) {
-    scores(0, sa);
-    const TileInfo ti = tile_info(0);
-    if (ti.mask) apply_mask(ti, sa);
-    rowmax(sa, ma);
-  }
-  for (int32_t n = 0; n < ntiles; n += 2) {
-    body(n, sa, ma, sb, mb);
-    if (n + 1 < ntiles) body(n + 1, sb, mb, sa, ma);
-  }
-
-#endif
 
   if (!wave_active) return;
 #pragma unroll
