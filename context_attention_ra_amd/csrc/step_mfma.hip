@@ -9,40 +9,40 @@
 // the k8ai page needs no special casing here.
 //
 // Design (CDNA4-first; FlashAttention is prior art, not the template):
-// * A workgroup is eight waves of 32 query rows (256 rows). Each K or V
-//   fragment a wave reads from LDS feeds one MFMA; on gfx950 the transposed
-//   LDS read of V runs at about half the rate of a plain 16-byte read.
-// * Keys stream through a kStages-deep LDS ring in tiles of kBK rows, fetched
-//   by bounds-checked buffer loads that write LDS directly (no staging
-//   registers; rows past the block read as zero). A tile is requested about
-//   three slots before it is consumed and waited for only just before, so
-//   global latency hides behind several slots.
+// * Work items are (batch*head slice, 256-row query tile). Workgroups are
+//   persistent, one per CU: each walks a list of items as one continuous
+//   stream of 64-key K/V tiles, so the loads of the next item's first tiles,
+//   and its queries, are in flight while the current item finishes. A
+//   workgroup that ran one item and exited would wait for its queries, state
+//   and first tiles with the CU idle, and all CUs would do so at the same
+//   time, contending for HBM.
+// * Eight waves of 32 query rows. Keys stream through a 4-deep LDS ring,
+//   fetched by bounds-checked buffer loads that write LDS directly (no
+//   staging registers; rows past the block read as zero).
 // * LDS holds each tile column-major in 16-byte columns; one load instruction
-//   fills a 1 KiB run (one or two columns), runs padded to 1088 bytes. Both the
-//   16-byte K reads and the transposed V reads are then free of bank
-//   conflicts, and every LDS address is a per-lane base plus an immediate.
+//   fills a 1 KiB run, runs padded to 1088 bytes. Both the 16-byte K reads and
+//   the transposed V reads are then free of bank conflicts, and every LDS
+//   address is a per-lane base plus an immediate.
 // * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //   the 32x32 accumulator layout gives every lane one query column and 16 of
 //   each 32 keys, so a row maximum is an in-lane reduction plus one 32-lane
 //   swap (v_permlane32_swap), and the per-query rescale factor is a lane scalar.
-// * Ping-pong: the two halves of the workgroup (one wave of each on every
-//   SIMD) alternate, one slot apart, between a matrix phase (scores of tile
-//   n+1 and PV of tile n) and a vector phase (mask, row maximum, rescale and
-//   exponentials), so one wave feeds the matrix core while the other computes
-//   exponentials; a workgroup barrier ends every slot.
 // * The probabilities stay in registers as the B operand of O^T += V^T P^T.
 //   The key order inside each 16-key MFMA slice is permuted to match the
 //   accumulator layout; the matching V^T operand is read with the gfx950
 //   transposing LDS load ds_read_b64_tr_b16, so P never leaves registers.
+// * Ping-pong: the two halves of the workgroup (one wave of each on every
+//   SIMD) alternate between a matrix phase and a vector phase, so one wave
+//   feeds the matrix core while the other computes exponentials.
 // * The running maximum only moves when a tile's maximum exceeds it by more
 //   than 2^8 in weight (lazy rescale); the state stays exact because O and l
 //   are always expressed relative to the same reference value m.
 // * Tiles whose keys all lie after the last query (causal) are never loaded;
 //   tiles straddling the diagonal, and ragged tails, are masked per element.
-// * Workgroup ids are remapped so that each of the 8 XCDs works through whole
-//   (batch, head) slices, keeping a slice's K/V block in that XCD's L2, and
-//   within a slice the query tiles at the end of the block (the heaviest under
-//   a causal mask and the zigzag split) start first.
+// * Each of the 8 XCDs owns a contiguous range of items (whole slices), so a
+//   slice's K/V block stays in that XCD's L2; within a slice the query tiles
+//   at the end (the heaviest under a causal mask and the zigzag split) come
+//   first, dealt to the XCD's workgroups in snake order to even out the work.
 
 #include "ra_device.h"
 #include "ra_launch.h"
@@ -51,16 +51,15 @@ namespace ra {
 namespace {
 
 constexpr int kWaves = 8;               // waves per workgroup
-constexpr int kQB = 1;                  // 32-row query blocks per wave
-constexpr int kBK = 64;                 // key rows per tile (32 or 64)
+constexpr int kBK = 64;                 // key rows per tile
 constexpr int kStages = 4;              // LDS ring depth
 constexpr int kAhead = 3;               // LDS operands read ahead of their MFMA
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBQ = 32 * kQB * kWaves;  // query rows per workgroup
+constexpr int kBQ = 32 * kWaves;        // query rows per work item
 constexpr int kNST = kBK / 32;          // 32-key halves per tile
 constexpr int kRun = 1088;              // LDS bytes per 1 KiB load run, padded
 constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
-static_assert(kBK == 32 || kBK == 64, "tile of 32 or 64 keys");
+constexpr int kXcds = 8;
 
 template <int D>
 struct Lay {
@@ -99,111 +98,142 @@ __device__ __forceinline__ bf16x4 lds_tr16(const char* p) {
 // s_waitcnt encodings (gfx9): wait until at most N vector-memory ops are pending
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// One work item: query tile qt0.. of slice prob, and the K/V tiles it sees
+// (two runs of tile indices: t0a.. (n0 tiles) and t1a.. (the rest)).
+struct Item {
+  int32_t prob, qt0, n0, t0a, t1a, ntiles;
+};
+
+// A position in a workgroup's stream of tiles: item number i of the
+// workgroup, the item, and the stream indices [g0, g1) of its tiles.
+struct Cursor {
+  int32_t i, g0, g1;
+  Item it;
+};
+
 template <int D, bool CAUSAL, bool FUSED>
 __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, int32_t init,
     float* __restrict__ Oacc, float* __restrict__ Mst, float* __restrict__ Lst,
-    bf16* __restrict__ Out, float* __restrict__ Lse, int32_t nqt, int32_t per_xcd) {
+    bf16* __restrict__ Out, float* __restrict__ Lse, int32_t nqt, int32_t per_xcd, int32_t nwg_x) {
   using L = Lay<D>;
   constexpr int KS = D / 16;  // k-steps of the score MFMA
   constexpr int DT = D / 32;  // 32-wide output tiles
   constexpr int NDMA = 2 * L::RUNS_PER_WAVE;  // load instructions per wave per tile
   __shared__ __attribute__((aligned(16))) char smem[kStages * L::STAGE];
 
-  // ---- which (slice, query tile) this workgroup owns
-  const int32_t total = nb * nqt;
-  const int32_t p = blockIdx.x;
-  const int32_t logical = (p & 7) * per_xcd + (p >> 3);
-  if (logical >= total) return;
-  const int32_t prob = logical / nqt;
-  const int32_t qtile = nqt - 1 - (logical - prob * nqt);
-  const int32_t qt0 = qtile * kBQ;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const size_t qbase = (size_t)prob * Lq * D;
-  const size_t kbase = (size_t)prob * Lk * D;
 
-  // this wave's query rows: block b covers rows w_r0 + 32b .. +31
-  const int32_t w_r0 = qt0 + 32 * kQB * w;
-  int32_t qrow[kQB], qpos[kQB];
-  bool qvalid[kQB];
-#pragma unroll
-  for (int b = 0; b < kQB; ++b) {
-    qrow[b] = w_r0 + 32 * b + l32;
-    qvalid[b] = qrow[b] < Lq;
-    qpos[b] = seg_pos(qs, qvalid[b] ? qrow[b] : Lq - 1);
-  }
+  // ---- this workgroup's items: XCD x owns logical items [x*per_xcd, ...);
+  // its nwg_x workgroups take them round by round, in snake order
+  const int32_t total = nb * nqt;
+  const int32_t xcd = blockIdx.x % kXcds, wj = blockIdx.x / kXcds;
+  const int32_t x_lo = xcd * per_xcd;
+  const int32_t x_cnt = max(0, min(per_xcd, total - x_lo));
+  const int32_t nrounds = (x_cnt + nwg_x - 1) / nwg_x;
+  auto item_logical = [&](int32_t i) -> int32_t {
+    const int32_t pos = (i & 1) ? (i + 1) * nwg_x - 1 - wj : i * nwg_x + wj;
+    return pos < x_cnt ? x_lo + pos : -1;
+  };
+  auto decode = [&](int32_t logical) {
+    Item it;
+    it.prob = logical / nqt;
+    const int32_t qtile = nqt - 1 - (logical - it.prob * nqt);
+    it.qt0 = qtile * kBQ;
+    // key rows this item can see: at most two row ranges
+    int32_t ra0 = 0, rb0 = Lk, ra1 = 0, rb1 = 0;
+    if (CAUSAL) {
+      int32_t qlo, qhi;
+      seg_range(qs, it.qt0, min(it.qt0 + kBQ, Lq), qlo, qhi);
+      (void)qlo;
+      auto vis = [&](int32_t start, int32_t n) {
+        int32_t x = qhi - start + 1;
+        return x < 0 ? 0 : (x > n ? n : x);
+      };
+      rb0 = vis(ks.start0, ks.len0);
+      ra1 = ks.len0;
+      rb1 = ks.len0 + (ks.len > ks.len0 ? vis(ks.start1, ks.len - ks.len0) : 0);
+    }
+    it.t0a = ra0 / kBK;
+    const int32_t t0b = (rb0 + kBK - 1) / kBK;
+    it.n0 = rb0 > ra0 ? t0b - it.t0a : 0;
+    it.t1a = ra1 / kBK;
+    const int32_t t1b = (rb1 + kBK - 1) / kBK;
+    if (it.n0 > 0 && it.t1a < t0b) it.t1a = t0b;
+    const int32_t n1 = rb1 > ra1 && t1b > it.t1a ? t1b - it.t1a : 0;
+    it.ntiles = it.n0 + n1;
+    return it;
+  };
+  auto tile_kt0 = [&](const Item& it, int32_t n) {
+    return (n < it.n0 ? it.t0a + n : it.t1a + (n - it.n0)) * kBK;
+  };
+  // the next item with at least one tile; g0 continues the stream
+  auto advance = [&](Cursor& c) {
+    c.g0 = c.g1;
+    for (++c.i; c.i < nrounds; ++c.i) {
+      const int32_t lg = item_logical(c.i);
+      if (lg < 0) continue;
+      c.it = decode(lg);
+      if (c.it.ntiles > 0) break;
+    }
+    c.g1 = c.g0 + (c.i < nrounds ? c.it.ntiles : 0);
+  };
 
-  const int32_t wg_r1 = min(qt0 + kBQ, Lq);
-  int32_t wg_qlo, wg_qhi;
-  seg_range(qs, qt0, wg_r1, wg_qlo, wg_qhi);
-  const bool wave_active = w_r0 < Lq;
-  int32_t w_qlo = 0, w_qhi = -1;
-  if (wave_active) seg_range(qs, w_r0, min(w_r0 + 32 * kQB, Lq), w_qlo, w_qhi);
-
-  // ---- key rows this workgroup can see: at most two row ranges
-  int32_t ra0 = 0, rb0 = Lk, ra1 = 0, rb1 = 0;
-  if (CAUSAL) {
-    auto vis = [&](int32_t start, int32_t n) {
-      int32_t x = wg_qhi - start + 1;
-      return x < 0 ? 0 : (x > n ? n : x);
-    };
-    rb0 = vis(ks.start0, ks.len0);
-    ra1 = ks.len0;
-    rb1 = ks.len0 + (ks.len > ks.len0 ? vis(ks.start1, ks.len - ks.len0) : 0);
-  }
-  const int32_t t0a = ra0 / kBK, t0b = (rb0 + kBK - 1) / kBK;
-  const int32_t n0 = rb0 > ra0 ? t0b - t0a : 0;
-  int32_t t1a = ra1 / kBK;
-  const int32_t t1b = (rb1 + kBK - 1) / kBK;
-  if (n0 > 0 && t1a < t0b) t1a = t0b;
-  const int32_t n1 = rb1 > ra1 && t1b > t1a ? t1b - t1a : 0;
-  const int32_t ntiles = n0 + n1;
-  auto tile_kt0 = [&](int32_t n) { return (n < n0 ? t0a + n : t1a + (n - n0)) * kBK; };
-
-  // ---- a query tile that sees no key of this block keeps its state: no
-  // loads and no stores, except that a first step stores the empty state
-  // (and a fused call the empty output: zeros, lse -inf)
-  if (ntiles == 0) {
-    if ((!FUSED && !init) || !wave_active) return;
+  // ---- items that see no key of the block keep their state: no loads and
+  // no stores, except that a first step stores the empty state (and a fused
+  // call the empty output: zeros, lse -inf). NT counts the stream's tiles.
+  int32_t NT = 0;
+  for (int32_t i = 0; i < nrounds; ++i) {
+    const int32_t lg = item_logical(i);
+    if (lg < 0) continue;
+    const Item it = decode(lg);
+    NT += it.ntiles;
+    if (it.ntiles > 0 || (!FUSED && !init)) continue;
+    const int32_t qrow = it.qt0 + 32 * w + l32;
+    if (qrow >= Lq) continue;
+    const size_t r = (size_t)it.prob * Lq + qrow;
+    if (FUSED) {
+      bf16* op = Out + r * D + 4 * h;
 #pragma unroll
-    for (int b = 0; b < kQB; ++b) {
-      if (!qvalid[b]) continue;
-      const size_t r = (size_t)prob * Lq + qrow[b];
-      if (FUSED) {
-        bf16* op = Out + qbase + (size_t)qrow[b] * D + 4 * h;
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+        for (int i4 = 0; i4 < 4; ++i4) *(bf16x4*)(op + 32 * t + 8 * i4) = bf16x4{};
+      if (Lse && h == 0) Lse[r] = kNegInf;
+    } else {
+      float* op = Oacc + r * D + 4 * h;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) *(bf16x4*)(op + 32 * t + 8 * i) = bf16x4{};
-        if (Lse && h == 0) Lse[r] = kNegInf;
-      } else {
-        float* op = Oacc + qbase + (size_t)qrow[b] * D + 4 * h;
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) *(f32x4*)(op + 32 * t + 8 * i) = f32x4{};
-        if (h == 0) {
-          Mst[r] = kNegInf;
-          Lst[r] = 0.f;
-        }
+        for (int i4 = 0; i4 < 4; ++i4) *(f32x4*)(op + 32 * t + 8 * i4) = f32x4{};
+      if (h == 0) {
+        Mst[r] = kNegInf;
+        Lst[r] = 0.f;
       }
     }
-    return;
   }
+  if (NT == 0) return;
 
-  // ---- K/V tiles: bounds-checked buffer loads straight into LDS. Load run r
-  // of a tile holds columns r, r+NRUN, ... of rows 0..kBK-1; lane i brings
+  Cursor first;
+  first.i = -1;
+  first.g1 = 0;
+  advance(first);
+
+  // ---- K/V tiles of the stream: tile g goes to stage g % kStages. Load run
+  // r of a tile holds columns r, r+NRUN, ... of rows 0..kBK-1; lane i brings
   // row i % kBK of column r + NRUN * (i / kBK). A wave owns RUNS_PER_WAVE runs.
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), 0, Lk * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + kbase), 0, Lk * D * 2, 0x00020000);
-  auto fetch = [&](int32_t n, int stage) {
-    const int32_t soff = tile_kt0(n) * D * 2;
-    char* sb = smem + stage * L::STAGE;
+  Cursor fc = first;  // item of the next tile to request
+  int32_t fg = 0;     // stream index of the next tile to request
+  auto fetch_next = [&]() {
+    if (fg == fc.g1) advance(fc);
+    const size_t kbase = (size_t)fc.it.prob * Lk * D;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), 0, Lk * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + kbase), 0, Lk * D * 2, 0x00020000);
+    const int32_t soff = tile_kt0(fc.it, fg - fc.g0) * D * 2;
+    char* sb = smem + (fg % kStages) * L::STAGE;
 #pragma unroll
     for (int i = 0; i < L::RUNS_PER_WAVE; ++i) {
       const int r = w * L::RUNS_PER_WAVE + i;
@@ -211,68 +241,114 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
       load_lds16(krs, sb + r * kRun, voff, soff);
       load_lds16(vrs, sb + L::TBYTES + r * kRun, voff, soff);
     }
+    ++fg;
   };
 
-  // the first tiles are requested before the Q and state loads
+  // the first tiles are requested before the query and state loads
 #pragma unroll
   for (int i = 0; i < kStages; ++i)
-    if (ntiles > i) fetch(i, i);
+    if (i < NT) fetch_next();
 
   // ---- query fragments: B operand of S^T = K Q^T (lane: query l32, d 16ks+8h..+8)
-  bf16x8 qf[kQB][KS];
+  bf16x8 qf[KS];
+  auto load_q = [&](const Item& it) {
+    const int32_t row = min(it.qt0 + 32 * w + l32, Lq - 1);
+    const bf16* qp = Q + ((size_t)it.prob * Lq + row) * D + 8 * h;
 #pragma unroll
-  for (int b = 0; b < kQB; ++b) {
-    const bf16* qp = Q + qbase + (size_t)(qvalid[b] ? qrow[b] : Lq - 1) * D + 8 * h;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[b][s] = *(const bf16x8*)(qp + 16 * s);
-  }
+    for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
+  };
+  load_q(first.it);
 
-  // ---- running state: O^T accumulators (lane: query l32, d 32dt+8i+4h+j)
-  f32x16 o[kQB][DT];
-  float mu[kQB];        // reference value in log2 units of the weights
-  float lpart[kQB][2];  // this lane's share of the row sum, two partial sums
+  // ---- running state of the current item: O^T accumulators (lane: query
+  // l32, d 32dt+8i+4h+j), reference value mu (log2 units), row-sum shares
+  f32x16 o[DT];
+  float mu;
+  float lpart[2];
+  Cursor cc = first;  // item whose state is in registers
+  int32_t qrow, qpos, w_qlo;
+  bool qvalid, wave_active;
+  auto begin_item = [&]() {
+    const Item& it = cc.it;
+    const int32_t w_r0 = it.qt0 + 32 * w;
+    qrow = w_r0 + l32;
+    qvalid = qrow < Lq;
+    qpos = seg_pos(qs, qvalid ? qrow : Lq - 1);
+    wave_active = w_r0 < Lq;
+    int32_t w_qhi;
+    w_qlo = 0;
+    if (wave_active) seg_range(qs, w_r0, min(w_r0 + 32, Lq), w_qlo, w_qhi);
 #pragma unroll
-  for (int b = 0; b < kQB; ++b) {
-#pragma unroll
-    for (int t = 0; t < DT; ++t) o[b][t] = f32x16{};
-    mu[b] = kNegInf;
-    lpart[b][0] = lpart[b][1] = 0.f;
-    if (!FUSED && !init && qvalid[b]) {
-      const float* op = Oacc + qbase + (size_t)qrow[b] * D + 4 * h;
+    for (int t = 0; t < DT; ++t) o[t] = f32x16{};
+    mu = kNegInf;
+    lpart[0] = lpart[1] = 0.f;
+    if (!FUSED && !init && qvalid) {
+      const size_t r = (size_t)it.prob * Lq + qrow;
+      const float* op = Oacc + r * D + 4 * h;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           f32x4 x = *(const f32x4*)(op + 32 * t + 8 * i);
-          o[b][t][4 * i + 0] = x[0];
-          o[b][t][4 * i + 1] = x[1];
-          o[b][t][4 * i + 2] = x[2];
-          o[b][t][4 * i + 3] = x[3];
+          o[t][4 * i + 0] = x[0];
+          o[t][4 * i + 1] = x[1];
+          o[t][4 * i + 2] = x[2];
+          o[t][4 * i + 3] = x[3];
         }
-      const size_t r = (size_t)prob * Lq + qrow[b];
-      mu[b] = Mst[r] * kLog2e;
-      lpart[b][0] = h == 0 ? Lst[r] : 0.f;
+      mu = Mst[r] * kLog2e;
+      lpart[0] = h == 0 ? Lst[r] : 0.f;
     }
-  }
+  };
+  auto end_item = [&]() {
+    const float lsum = partner32_sum(lpart[0] + lpart[1]);
+    if (!wave_active || !qvalid) return;
+    const size_t r = (size_t)cc.it.prob * Lq + qrow;
+    if (FUSED) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      bf16* op = Out + r * D + 4 * h;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x4 y = {to_bf16(o[t][4 * i + 0] * inv), to_bf16(o[t][4 * i + 1] * inv),
+                      to_bf16(o[t][4 * i + 2] * inv), to_bf16(o[t][4 * i + 3] * inv)};
+          *(bf16x4*)(op + 32 * t + 8 * i) = y;
+        }
+      if (Lse && h == 0) Lse[r] = lsum > 0.f ? (mu + fast_log2(lsum)) * kLn2 : kNegInf;
+    } else {
+      float* op = Oacc + r * D + 4 * h;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 y = {o[t][4 * i + 0], o[t][4 * i + 1], o[t][4 * i + 2], o[t][4 * i + 3]};
+          *(f32x4*)(op + 32 * t + 8 * i) = y;
+        }
+      if (h == 0) {
+        Mst[r] = mu * kLn2;
+        Lst[r] = lsum;
+      }
+    }
+  };
+  begin_item();
 
   // per-lane LDS read bases within a stage; the rest are immediate offsets.
   // K (A operand): row 32st+l32, column 2ksi+h.
   // V^T (transposed reads): row 16kc+4(g>>1)+rr(+8), columns 32t+16(g&1)+4cc..+3
-  // (16-byte column 4t+2(g&1)+(cc>>1), byte 8(cc&1)).
-  const int g = lane >> 4, jj = lane & 15, rr = jj >> 2, cc = jj & 3;
+  // (16-byte column 4t+2(g&1)+(c4>>1), byte 8(c4&1)).
+  const int g = lane >> 4, jj = lane & 15, rr = jj >> 2, c4 = jj & 3;
   const int kread = L::at(l32, h);
-  const int vread = L::TBYTES + L::at(4 * (g >> 1) + rr, 2 * (g & 1) + (cc >> 1)) + 8 * (cc & 1);
+  const int vread = L::TBYTES + L::at(4 * (g >> 1) + rr, 2 * (g & 1) + (c4 >> 1)) + 8 * (c4 & 1);
 
-  // per-tile facts for this wave
+  // per-tile facts for this wave (stream tile m of the current item)
   struct TileInfo {
     int32_t kt0;
     bool mask;       // element mask needed (diagonal, ragged tail, or fully after the queries)
     bool straddle;   // tile crosses the K segment boundary
     int32_t kpos0;   // global position of the tile's first row (if not straddling)
   };
-  auto tile_info = [&](int32_t n) {
+  auto tile_info = [&](int32_t m) {
     TileInfo ti;
-    ti.kt0 = tile_kt0(n);
+    ti.kt0 = tile_kt0(cc.it, m - cc.g0);
     const int32_t kend = min(ti.kt0 + kBK, Lk);
     ti.mask = ti.kt0 + kBK > Lk;
     ti.straddle = ti.kt0 < ks.len0 && kend > ks.len0;
@@ -286,135 +362,114 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     return ti;
   };
 
-  typedef f32x16 Scores[kQB][kNST];  // [query block][32-key part of the tile]
+  typedef f32x16 Scores[kNST];   // [32-key part of the tile]
+  typedef bf16x8 Probs[2 * kNST];  // [16-key slice]
+  Scores sc;
+  Probs pf;
 
-  auto scores = [&](int stage, Scores& s) {
+  auto scores = [&](int stage) {
     const char* kb = smem + stage * L::STAGE + kread;
 #pragma unroll
-    for (int b = 0; b < kQB; ++b)
-#pragma unroll
-      for (int st = 0; st < kNST; ++st) s[b][st] = f32x16{};
+    for (int st = 0; st < kNST; ++st) sc[st] = f32x16{};
 #pragma unroll
     for (int ksi = 0; ksi < KS; ++ksi)
 #pragma unroll
       for (int st = 0; st < kNST; ++st) {
         // rows 32st+l32, column 2ksi+h: the lane base covers l32 and h
         const bf16x8 kf = lds_b128(kb + L::at(32 * st, 2 * ksi));
-#pragma unroll
-        for (int b = 0; b < kQB; ++b)
-          s[b][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[b][ksi], s[b][st], 0, 0, 0);
+        sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ksi], sc[st], 0, 0, 0);
       }
   };
 
-  auto apply_mask = [&](const TileInfo& ti, Scores& s) {
+  auto apply_mask = [&](const TileInfo& ti) {
+    if (!ti.straddle) {
+      // key offset e in the tile is visible iff e <= lim
+      int32_t lim = Lk - 1 - ti.kt0;
+      if (CAUSAL) lim = min(lim, qpos - ti.kpos0);
 #pragma unroll
-    for (int b = 0; b < kQB; ++b) {
-      if (!ti.straddle) {
-        // key offset e in the tile is visible iff e <= lim
-        int32_t lim = Lk - 1 - ti.kt0;
-        if (CAUSAL) lim = min(lim, qpos[b] - ti.kpos0);
+      for (int st = 0; st < kNST; ++st)
 #pragma unroll
-        for (int st = 0; st < kNST; ++st)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < 4; ++j) {
+            const int e = 32 * st + 8 * i + 4 * h + j;
+            sc[st][4 * i + j] = e > lim ? kNegInf : sc[st][4 * i + j];
+          }
+    } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int e = 32 * st + 8 * i + 4 * h + j;
-              s[b][st][4 * i + j] = e > lim ? kNegInf : s[b][st][4 * i + j];
-            }
-      } else {
+      for (int st = 0; st < kNST; ++st)
 #pragma unroll
-        for (int st = 0; st < kNST; ++st)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int32_t kr = ti.kt0 + 32 * st + 8 * i + 4 * h + j;
-              const bool m = kr >= Lk || (CAUSAL && seg_pos(ks, kr) > qpos[b]);
-              s[b][st][4 * i + j] = m ? kNegInf : s[b][st][4 * i + j];
-            }
-      }
+          for (int j = 0; j < 4; ++j) {
+            const int32_t kr = ti.kt0 + 32 * st + 8 * i + 4 * h + j;
+            const bool m = kr >= Lk || (CAUSAL && seg_pos(ks, kr) > qpos);
+            sc[st][4 * i + j] = m ? kNegInf : sc[st][4 * i + j];
+          }
     }
   };
 
-  // row maxima of one tile's scores, log2 units (both lanes of a query agree)
-  auto rowmax = [&](const Scores& s, float (&mt)[kQB]) {
+  // row maximum of one tile's scores, log2 units (both lanes of a query agree)
+  auto rowmax = [&]() {
+    // 16*kNST values: chains of v_max3, two values per instruction
+    float a[4];
 #pragma unroll
-    for (int b = 0; b < kQB; ++b) {
-      // 16*kNST values: chains of v_max3, two values per instruction
-      float a[4];
+    for (int c = 0; c < 4; ++c) {
+      a[c] = max2_nn(sc[0][4 * c], sc[0][4 * c + 1]);
+      a[c] = max3_nn(a[c], sc[0][4 * c + 2], sc[0][4 * c + 3]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        a[c] = max2_nn(s[b][0][4 * c], s[b][0][4 * c + 1]);
-        a[c] = max3_nn(a[c], s[b][0][4 * c + 2], s[b][0][4 * c + 3]);
-#pragma unroll
-        for (int st = 1; st < kNST; ++st) {
-          a[c] = max3_nn(a[c], s[b][st][4 * c], s[b][st][4 * c + 1]);
-          a[c] = max3_nn(a[c], s[b][st][4 * c + 2], s[b][st][4 * c + 3]);
-        }
+      for (int st = 1; st < kNST; ++st) {
+        a[c] = max3_nn(a[c], sc[st][4 * c], sc[st][4 * c + 1]);
+        a[c] = max3_nn(a[c], sc[st][4 * c + 2], sc[st][4 * c + 3]);
       }
-      mt[b] = partner32_max(max3_nn(max2_nn(a[0], a[1]), a[2], a[3])) * c_log2;
     }
+    return partner32_max(max3_nn(max2_nn(a[0], a[1]), a[2], a[3])) * c_log2;
   };
 
   // the (rare) rescale of the state when a tile's maximum outgrows the
   // reference value by more than kTau
-  auto rescale = [&](const float (&mt)[kQB]) {
+  auto rescale = [&](float mt) {
+    const bool need = mt > mu + kTau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      // lanes keeping their reference (also rows with no visible key yet,
+      // mu = -inf) must get exactly 1, not exp2(-inf - -inf)
+      const float mnew = need ? mt : mu;
+      const float alpha = need ? fast_exp2(mu - mnew) : 1.f;
+      lpart[0] *= alpha;
+      lpart[1] *= alpha;
 #pragma unroll
-    for (int b = 0; b < kQB; ++b) {
-      const bool need = mt[b] > mu[b] + kTau;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        // lanes keeping their reference (also rows with no visible key yet,
-        // mu = -inf) must get exactly 1, not exp2(-inf - -inf)
-        const float mnew = need ? mt[b] : mu[b];
-        const float alpha = need ? fast_exp2(mu[b] - mnew) : 1.f;
-        lpart[b][0] *= alpha;
-        lpart[b][1] *= alpha;
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[b][t][r] *= alpha;
-        mu[b] = mnew;
-      }
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      mu = mnew;
     }
   };
-
-  typedef bf16x8 Probs[kQB][2 * kNST];  // [query block][16-key slice]
 
   // exponentials of one tile into bf16 B operands (and the row-sum shares,
   // summed in fp32 before rounding so that lse keeps full precision)
-  auto exps = [&](const Scores& s, Probs& pf) {
+  auto exps = [&]() {
+    const float mus = mu == kNegInf ? 0.f : mu;
 #pragma unroll
-    for (int b = 0; b < kQB; ++b) {
-      const float mus = mu[b] == kNegInf ? 0.f : mu[b];
+    for (int st = 0; st < kNST; ++st)
 #pragma unroll
-      for (int st = 0; st < kNST; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(__builtin_fmaf(s[b][st][r], c_log2, -mus));
-          lpart[b][r & 1] += pr;
-          pf[b][2 * st + r / 8][r % 8] = to_bf16(pr);
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const float pr = fast_exp2(__builtin_fmaf(sc[st][r], c_log2, -mus));
+        lpart[r & 1] += pr;
+        pf[2 * st + r / 8][r % 8] = to_bf16(pr);
+      }
   };
-
-
 
   // The matrix phase of one tile in a fixed order: the score MFMAs of the next
   // tile, then the PV MFMAs of this one. Each step's LDS operand is read
   // kAhead steps earlier and scheduling barriers keep that order, so no MFMA
   // waits on a just-issued LDS read.
-  Scores sc;
-  Probs pf;
   auto mfma_phase = [&](int kstage, int vstage) {
     constexpr int NSC = KS * kNST;      // score steps
     constexpr int NPV = 2 * kNST * DT;  // PV steps
     const char* kb = smem + kstage * L::STAGE + kread;
     const char* vb = smem + vstage * L::STAGE + vread;
 #pragma unroll
-    for (int b = 0; b < kQB; ++b)
-#pragma unroll
-      for (int st = 0; st < kNST; ++st) sc[b][st] = f32x16{};
+    for (int st = 0; st < kNST; ++st) sc[st] = f32x16{};
     auto operand = [&](int i) -> bf16x8 {
       if (i < NSC) return lds_b128(kb + L::at(32 * (i % kNST), 2 * (i / kNST)));
       const int j = i - NSC, off = L::at(16 * (j / DT), 4 * (j % DT));
@@ -430,134 +485,132 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
       const bf16x8 cur = op[i % kAhead];
       if (i < NSC) {
         const int st = i % kNST, ksi = i / kNST;
-#pragma unroll
-        for (int b = 0; b < kQB; ++b)
-          sc[b][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[b][ksi], sc[b][st], 0, 0, 0);
+        sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ksi], sc[st], 0, 0, 0);
       } else {
         const int j = i - NSC, kc = j / DT, t = j % DT;
-#pragma unroll
-        for (int b = 0; b < kQB; ++b)
-          o[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[b][kc], o[b][t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[kc], o[t], 0, 0, 0);
       }
       if (i + kAhead < NSC + NPV) op[i % kAhead] = operand(i + kAhead);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- ping-pong schedule. The two halves of the workgroup (waves 0..W/2-1
-  // and W/2..W-1, one of each on every SIMD) run the same per-tile program
-  // shifted by half an iteration: while one wave of a SIMD issues its matrix
-  // work (scores of tile n+1 and PV of tile n), the other does its vector
-  // work (mask, row maximum, rescale and exponentials of its next tile), so
-  // the matrix core always has a wave feeding it. Time advances in slots that
-  // end with a workgroup barrier:
+  // softmax of stream tile m of the current item (scores in sc)
+  auto vector_phase = [&](int32_t m) {
+    const TileInfo ti = tile_info(m);
+    if (ti.mask) apply_mask(ti);
+    rescale(rowmax());
+    exps();
+  };
+
+  // ---- ping-pong schedule, one item at a time. The two halves of the
+  // workgroup (waves 0..3 and 4..7, one of each on every SIMD) run the same
+  // per-tile program shifted by one slot: while one wave of a SIMD issues its
+  // matrix work (scores of tile n+1 and PV of tile n), the other does its
+  // vector work (mask, row maximum, rescale and exponentials of its next
+  // tile). Time advances in slots that end with a workgroup barrier:
   //   group A: slot 0 = start (scores + softmax of tile 0), then slot 2n+1 =
-  //            matrix phase n, slot 2n+2 = vector phase n;
+  //            matrix phase n, slot 2n+2 = vector phase of tile n+1;
   //   group B: the same, one slot later.
-  // The matrix phase n reads K of tile n+1 and V of tile n, so tile m is
-  // needed from slot 2m-1 and free after slot 2m+2: tile m+kStages is
-  // requested at the start of slot 2m+3 into m's stage, and tile n+1 is
-  // waited for at the end of slot 2n.
+  // Tiles are numbered along the stream (g = g0 + n) and tile g sits in
+  // stage g % kStages. The matrix phase n reads K of tile n+1 and V of tile n,
+  // so tile g is needed from slot 2n-1 and free after slot 2n+2 of its item:
+  // at the start of odd slot 2m+3 (m >= -1) the stream tile g0+m+4 is
+  // requested into the stage of tile g0+m, which may already belong to the
+  // next item, so the next item's first tiles land while this one finishes.
+  // Tile n+1 is waited for at the end of slot 2n; at an item boundary
+  // everything in flight (queries, state, tiles) is waited for.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // group B: waves w and w + 4 share a SIMD
-  const bool late = w >= kWaves / 2;
-  auto vector_phase = [&](int32_t n) {  // softmax of tile n (scores in sc)
-    const TileInfo ti = tile_info(n);
-    if (ti.mask) apply_mask(ti, sc);
-    float mt[kQB];
-    rowmax(sc, mt);
-    rescale(mt);
-    exps(sc, pf);
-  };
-  const int32_t nslots = ntiles > 0 ? 2 * ntiles + 1 : 0;
-  for (int32_t s = 0; s < nslots; ++s) {
-    if ((s & 1) && s >= 3) {
-      const int32_t m = (s - 3) >> 1;
-      if (m + kStages < ntiles) fetch(m + kStages, m % kStages);
-    }
-    const int32_t a = late ? s - 1 : s;  // this group's own slot number
-    if (a == 0) {
-      scores(0, sc);
-      vector_phase(0);
-    } else if (a > 0 && (a & 1)) {
-      const int32_t n = (a - 1) >> 1;
-      if (n < ntiles) {
-        __builtin_amdgcn_s_setprio(1);
-        // past the last tile the scores read a stale stage and are never used
-        mfma_phase((n + 1) % kStages, n % kStages);
-        __builtin_amdgcn_s_setprio(0);
+  const bool late = w >= kWaves / 2;  // group B
+  for (;;) {
+    const int32_t g0 = cc.g0, nt = cc.g1 - cc.g0;
+    const int32_t nslots = 2 * nt + 1;
+    for (int32_t s = 0; s < nslots; ++s) {
+      if (s & 1) {
+        const int32_t target = g0 + ((s - 3) >> 1) + kStages;
+        if (fg == target && fg < NT) fetch_next();
       }
-    } else if (a > 0) {
-      const int32_t n = (a - 2) >> 1;
-      if (n + 1 < ntiles) vector_phase(n + 1);
+      const int32_t a = late ? s - 1 : s;  // this group's own slot number
+      if (a == 0) {
+        scores(g0 % kStages);
+        vector_phase(g0);
+      } else if (a > 0 && (a & 1)) {
+        const int32_t n = (a - 1) >> 1;
+        if (n < nt) {
+          __builtin_amdgcn_s_setprio(1);
+          // past the item's last tile the scores read a stage that is not
+          // this item's and are never used
+          mfma_phase((g0 + n + 1) % kStages, (g0 + n) % kStages);
+          __builtin_amdgcn_s_setprio(0);
+        }
+      } else if (a > 0) {
+        const int32_t n = (a - 2) >> 1;
+        if (n + 1 < nt) vector_phase(g0 + n + 1);
+      }
+      if (!(s & 1)) {
+        // end of slot 2n: stream tile g0+n+1 must be in LDS; tiles
+        // requested after it may stay in flight
+        const int32_t n = s >> 1;
+        const int32_t in_flight = fg - (g0 + n + 2);
+        if (in_flight >= 2)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA));
+        else if (in_flight == 1)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      __syncthreads();
     }
-    if (!(s & 1)) {
-      // end of slot 2n: tile n+1 must be in LDS; tiles requested later may
-      // stay in flight
-      const int32_t n = s >> 1;
-      const int32_t latest = min(ntiles - 1, n + kStages - 2);  // requested so far
-      const int32_t in_flight = latest - (n + 1);
-      if (in_flight >= 2)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA));
-      else if (in_flight == 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // queries first (theirs is the longest wait), then this item's results,
+    // then the next item's state
+    const bool more = cc.g1 < NT;
+    Cursor nx = cc;
+    if (more) {
+      advance(nx);
+      load_q(nx.it);
+      // the compiler cannot tell which iteration reloaded the query
+      // registers: without this wait it would wait for every outstanding load
+      // before each score product
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
+    end_item();
+    if (!more) break;
+    cc = nx;
+    begin_item();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-  }
-
-
-  if (!wave_active) return;
-#pragma unroll
-  for (int b = 0; b < kQB; ++b) {
-    const float lsum = partner32_sum(lpart[b][0] + lpart[b][1]);
-    if (!qvalid[b]) continue;
-    if (FUSED) {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      bf16* op = Out + qbase + (size_t)qrow[b] * D + 4 * h;
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x4 y = {to_bf16(o[b][t][4 * i + 0] * inv), to_bf16(o[b][t][4 * i + 1] * inv),
-                      to_bf16(o[b][t][4 * i + 2] * inv), to_bf16(o[b][t][4 * i + 3] * inv)};
-          *(bf16x4*)(op + 32 * t + 8 * i) = y;
-        }
-      if (Lse && h == 0)
-        Lse[(size_t)prob * Lq + qrow[b]] = lsum > 0.f ? (mu[b] + fast_log2(lsum)) * kLn2 : kNegInf;
-    } else {
-      float* op = Oacc + qbase + (size_t)qrow[b] * D + 4 * h;
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 y = {o[b][t][4 * i + 0], o[b][t][4 * i + 1], o[b][t][4 * i + 2], o[b][t][4 * i + 3]};
-          *(f32x4*)(op + 32 * t + 8 * i) = y;
-        }
-      if (h == 0) {
-        const size_t r = (size_t)prob * Lq + qrow[b];
-        Mst[r] = mu[b] * kLn2;
-        Lst[r] = lsum;
-      }
-    }
   }
 }
 
 DevSegs dev(const HostSegs& s) { return DevSegs{s.start0, s.start1, s.len0, s.len}; }
 
+// workgroups per XCD: one per CU (a workgroup's LDS ring fills a CU)
+int32_t cus_per_xcd() {
+  static int32_t n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < kXcds)
+      cus = 256;
+    n = cus / kXcds;
+  }
+  return n;
+}
+
 template <int D, bool CAUSAL, bool FUSED>
 hipError_t launch(const StepArgs& a, bf16* out, float* lse, hipStream_t st) {
   const int32_t nqt = (a.Lq + kBQ - 1) / kBQ;
   const int64_t total = (int64_t)a.nb * nqt;
-  const int32_t per_xcd = (int32_t)((total + 7) / 8);
+  const int32_t per_xcd = (int32_t)((total + kXcds - 1) / kXcds);
+  const int32_t nwg_x = min(per_xcd, cus_per_xcd());
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((step_mfma_kernel<D, CAUSAL, FUSED>), dim3(8 * per_xcd), dim3(kThreads), 0,
+  hipLaunchKernelGGL((step_mfma_kernel<D, CAUSAL, FUSED>), dim3(kXcds * nwg_x), dim3(kThreads), 0,
                      st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.nb, a.Lq, a.Lk,
                      dev(a.qs), dev(a.ks), c, (int32_t)a.init, a.o_acc, a.m, a.l, out, lse, nqt,
-                     per_xcd);
+                     per_xcd, nwg_x);
   return hipGetLastError();
 }
 
