@@ -98,6 +98,15 @@ __device__ __forceinline__ bf16x4 lds_tr16(const char* p) {
 // s_waitcnt encodings (gfx9): wait until at most N vector-memory ops are pending
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// The kernel body is written as lambdas; with two copies of the schedule the
+// inliner would otherwise turn some of them into calls with stack frames.
+#define RA_INLINE __attribute__((always_inline))
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 // One work item: query tile qt0.. of slice prob, and the K/V tiles it sees
 // (two runs of tile indices: t0a.. (n0 tiles) and t1a.. (the rest)).
 struct Item {
@@ -133,11 +142,11 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   const int32_t x_lo = xcd * per_xcd;
   const int32_t x_cnt = max(0, min(per_xcd, total - x_lo));
   const int32_t nrounds = (x_cnt + nwg_x - 1) / nwg_x;
-  auto item_logical = [&](int32_t i) -> int32_t {
+  auto item_logical = [&](int32_t i) RA_INLINE -> int32_t {
     const int32_t pos = (i & 1) ? (i + 1) * nwg_x - 1 - wj : i * nwg_x + wj;
     return pos < x_cnt ? x_lo + pos : -1;
   };
-  auto decode = [&](int32_t logical) {
+  auto decode = [&](int32_t logical) RA_INLINE {
     Item it;
     it.prob = logical / nqt;
     const int32_t qtile = nqt - 1 - (logical - it.prob * nqt);
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
       int32_t qlo, qhi;
       seg_range(qs, it.qt0, min(it.qt0 + kBQ, Lq), qlo, qhi);
       (void)qlo;
-      auto vis = [&](int32_t start, int32_t n) {
+      auto vis = [&](int32_t start, int32_t n) RA_INLINE {
         int32_t x = qhi - start + 1;
         return x < 0 ? 0 : (x > n ? n : x);
       };
@@ -166,11 +175,11 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     it.ntiles = it.n0 + n1;
     return it;
   };
-  auto tile_kt0 = [&](const Item& it, int32_t n) {
+  auto tile_kt0 = [&](const Item& it, int32_t n) RA_INLINE {
     return (n < it.n0 ? it.t0a + n : it.t1a + (n - it.n0)) * kBK;
   };
   // the next item with at least one tile; g0 continues the stream
-  auto advance = [&](Cursor& c) {
+  auto advance = [&](Cursor& c) RA_INLINE {
     c.g0 = c.g1;
     for (++c.i; c.i < nrounds; ++c.i) {
       const int32_t lg = item_logical(c.i);
@@ -225,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   // row i % kBK of column r + NRUN * (i / kBK). A wave owns RUNS_PER_WAVE runs.
   Cursor fc = first;  // item of the next tile to request
   int32_t fg = 0;     // stream index of the next tile to request
-  auto fetch_next = [&]() {
+  auto fetch_next = [&]() RA_INLINE {
     if (fg == fc.g1) advance(fc);
     const size_t kbase = (size_t)fc.it.prob * Lk * D;
     const __amdgpu_buffer_rsrc_t krs =
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
 
   // ---- query fragments: B operand of S^T = K Q^T (lane: query l32, d 16ks+8h..+8)
   bf16x8 qf[KS];
-  auto load_q = [&](const Item& it) {
+  auto load_q = [&](const Item& it) RA_INLINE {
     const int32_t row = min(it.qt0 + 32 * w + l32, Lq - 1);
     const bf16* qp = Q + ((size_t)it.prob * Lq + row) * D + 8 * h;
 #pragma unroll
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   Cursor cc = first;  // item whose state is in registers
   int32_t qrow, qpos, w_qlo;
   bool qvalid, wave_active;
-  auto begin_item = [&]() {
+  auto begin_item = [&]() RA_INLINE {
     const Item& it = cc.it;
     const int32_t w_r0 = it.qt0 + 32 * w;
     qrow = w_r0 + l32;
@@ -277,6 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     int32_t w_qhi;
     w_qlo = 0;
     if (wave_active) seg_range(qs, w_r0, min(w_r0 + 32, Lq), w_qlo, w_qhi);
+    w_qlo = __builtin_amdgcn_readfirstlane(w_qlo);  // the same in every lane
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = f32x16{};
     mu = kNegInf;
@@ -298,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
       lpart[0] = h == 0 ? Lst[r] : 0.f;
     }
   };
-  auto end_item = [&]() {
+  auto end_item = [&]() RA_INLINE {
     const float lsum = partner32_sum(lpart[0] + lpart[1]);
     if (!wave_active || !qvalid) return;
     const size_t r = (size_t)cc.it.prob * Lq + qrow;
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     bool straddle;   // tile crosses the K segment boundary
     int32_t kpos0;   // global position of the tile's first row (if not straddling)
   };
-  auto tile_info = [&](int32_t m) {
+  auto tile_info = [&](int32_t m) RA_INLINE {
     TileInfo ti;
     ti.kt0 = tile_kt0(cc.it, m - cc.g0);
     const int32_t kend = min(ti.kt0 + kBK, Lk);
@@ -367,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   Scores sc;
   Probs pf;
 
-  auto scores = [&](int stage) {
+  auto scores = [&](int stage) RA_INLINE {
     const char* kb = smem + stage * L::STAGE + kread;
 #pragma unroll
     for (int st = 0; st < kNST; ++st) sc[st] = f32x16{};
@@ -381,28 +391,36 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
       }
   };
 
-  auto apply_mask = [&](const TileInfo& ti) {
+  auto apply_mask = [&](const TileInfo& ti) RA_INLINE {
     if (!ti.straddle) {
       // key offset e in the tile is visible iff e <= lim
       int32_t lim = Lk - 1 - ti.kt0;
       if (CAUSAL) lim = min(lim, qpos - ti.kpos0);
+      // compare the lane-independent part of e with a per-lane limit, so that
+      // the 32 offsets are immediates rather than registers
+      const int32_t limh = lim - 4 * h;
 #pragma unroll
       for (int st = 0; st < kNST; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int e = 32 * st + 8 * i + 4 * h + j;
-            sc[st][4 * i + j] = e > lim ? kNegInf : sc[st][4 * i + j];
+            const int e = 32 * st + 8 * i + j;  // + 4h
+            sc[st][4 * i + j] = e > limh ? kNegInf : sc[st][4 * i + j];
           }
     } else {
+      // only the tile holding the segment boundary straddles it; an opaque
+      // copy of its start keeps the compiler from computing this tile's 32
+      // masks ahead for every item and holding them in scalar registers
+      int32_t kt0 = ti.kt0;
+      asm volatile("" : "+v"(kt0));
 #pragma unroll
       for (int st = 0; st < kNST; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int32_t kr = ti.kt0 + 32 * st + 8 * i + 4 * h + j;
+            const int32_t kr = kt0 + 32 * st + 8 * i + 4 * h + j;
             const bool m = kr >= Lk || (CAUSAL && seg_pos(ks, kr) > qpos);
             sc[st][4 * i + j] = m ? kNegInf : sc[st][4 * i + j];
           }
@@ -410,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   };
 
   // row maximum of one tile's scores, log2 units (both lanes of a query agree)
-  auto rowmax = [&]() {
+  auto rowmax = [&]() RA_INLINE {
     // 16*kNST values: chains of v_max3, two values per instruction
     float a[4];
 #pragma unroll
@@ -428,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
 
   // the (rare) rescale of the state when a tile's maximum outgrows the
   // reference value by more than kTau
-  auto rescale = [&](float mt) {
+  auto rescale = [&](float mt) RA_INLINE {
     const bool need = mt > mu + kTau;
     if (__builtin_amdgcn_ballot_w64(need)) {
       // lanes keeping their reference (also rows with no visible key yet,
@@ -447,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
 
   // exponentials of one tile into bf16 B operands (and the row-sum shares,
   // summed in fp32 before rounding so that lse keeps full precision)
-  auto exps = [&]() {
+  auto exps = [&]() RA_INLINE {
     const float mus = mu == kNegInf ? 0.f : mu;
 #pragma unroll
     for (int st = 0; st < kNST; ++st)
@@ -463,14 +481,14 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   // tile, then the PV MFMAs of this one. Each step's LDS operand is read
   // kAhead steps earlier and scheduling barriers keep that order, so no MFMA
   // waits on a just-issued LDS read.
-  auto mfma_phase = [&](int kstage, int vstage) {
+  auto mfma_phase = [&](int kstage, int vstage) RA_INLINE {
     constexpr int NSC = KS * kNST;      // score steps
     constexpr int NPV = 2 * kNST * DT;  // PV steps
     const char* kb = smem + kstage * L::STAGE + kread;
     const char* vb = smem + vstage * L::STAGE + vread;
 #pragma unroll
     for (int st = 0; st < kNST; ++st) sc[st] = f32x16{};
-    auto operand = [&](int i) -> bf16x8 {
+    auto operand = [&](int i) RA_INLINE -> bf16x8 {
       if (i < NSC) return lds_b128(kb + L::at(32 * (i % kNST), 2 * (i / kNST)));
       const int j = i - NSC, off = L::at(16 * (j / DT), 4 * (j % DT));
       const bf16x4 va = lds_tr16(vb + off);
@@ -496,11 +514,15 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   };
 
   // softmax of stream tile m of the current item (scores in sc)
-  auto vector_phase = [&](int32_t m) {
+  auto vector_phase = [&](int32_t m) RA_INLINE {
     const TileInfo ti = tile_info(m);
     if (ti.mask) apply_mask(ti);
     rescale(rowmax());
     exps();
+    // the weights are complete here: without this use the compiler sinks part
+    // of the exponentials and conversions past the barrier into the other
+    // phase, where the same wave then issues them between its products
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]), "v"(lpart[0]), "v"(lpart[1]));
   };
 
   // ---- ping-pong schedule, one item at a time. The two halves of the
@@ -523,45 +545,56 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  const bool late = w >= kWaves / 2;  // group B
+  // One copy of the schedule per group, the group a compile-time constant: a
+  // group is made of whole waves, but the compiler cannot prove it, and a group
+  // flag known only at run time would put the slot arithmetic on the vector
+  // unit.
+  auto run = [&](auto group) RA_INLINE {
+  constexpr bool late = decltype(group)::value;  // group B
   for (;;) {
     const int32_t g0 = cc.g0, nt = cc.g1 - cc.g0;
-    const int32_t nslots = 2 * nt + 1;
-    for (int32_t s = 0; s < nslots; ++s) {
-      if (s & 1) {
-        const int32_t target = g0 + ((s - 3) >> 1) + kStages;
-        if (fg == target && fg < NT) fetch_next();
-      }
-      const int32_t a = late ? s - 1 : s;  // this group's own slot number
-      if (a == 0) {
-        scores(g0 % kStages);
-        vector_phase(g0);
-      } else if (a > 0 && (a & 1)) {
-        const int32_t n = (a - 1) >> 1;
-        if (n < nt) {
-          __builtin_amdgcn_s_setprio(1);
-          // past the item's last tile the scores read a stage that is not
-          // this item's and are never used
-          mfma_phase((g0 + n + 1) % kStages, (g0 + n) % kStages);
-          __builtin_amdgcn_s_setprio(0);
-        }
-      } else if (a > 0) {
-        const int32_t n = (a - 2) >> 1;
-        if (n + 1 < nt) vector_phase(g0 + n + 1);
-      }
-      if (!(s & 1)) {
-        // end of slot 2n: stream tile g0+n+1 must be in LDS; tiles
-        // requested after it may stay in flight
-        const int32_t n = s >> 1;
-        const int32_t in_flight = fg - (g0 + n + 2);
-        if (in_flight >= 2)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA));
-        else if (in_flight == 1)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
-        else
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // end of slot 2n: stream tile g0+n+1 must be in LDS; tiles requested
+    // after it may stay in flight
+    auto slot_end = [&](int32_t n) RA_INLINE {
+      const int32_t in_flight = fg - (g0 + n + 2);
+      if (in_flight >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA));
+      else if (in_flight == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+    };
+    auto matrix = [&](int32_t n) RA_INLINE {
+      __builtin_amdgcn_s_setprio(1);
+      mfma_phase((g0 + n + 1) % kStages, (g0 + n) % kStages);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // slot 0: group A starts
+    if (!late) {
+      scores(g0 % kStages);
+      vector_phase(g0);
+    }
+    slot_end(0);
+    // slots 2n+1 and 2n+2. The slot arithmetic is the same for both groups;
+    // only the choice of phase depends on the group, a whole wave.
+    for (int32_t n = 0; n < nt; ++n) {
+      if (fg == g0 + n - 1 + kStages && fg < NT) fetch_next();
+      if (!late) {
+        // past the item's last tile the scores read a stage that is not
+        // this item's and are never used
+        matrix(n);
+      } else {
+        if (n == 0) scores(g0 % kStages);  // group B starts
+        vector_phase(g0 + n);
       }
       __syncthreads();
+      if (!late) {
+        if (n + 1 < nt) vector_phase(g0 + n + 1);
+      } else {
+        matrix(n);
+      }
+      slot_end(n + 1);
     }
     // queries first (theirs is the longest wait), then this item's results,
     // then the next item's state
@@ -582,6 +615,11 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   }
+  };
+  if (w >= kWaves / 2)
+    run(BoolC<true>{});
+  else
+    run(BoolC<false>{});
 }
 
 DevSegs dev(const HostSegs& s) { return DevSegs{s.start0, s.start1, s.len0, s.len}; }
