@@ -21,7 +21,7 @@ RA_MASK_NONE, RA_MASK_CAUSAL = 0, 1
 RA_STEP_INIT = 1
 
 # every symbol include/ra.h declares
-EXPORTS = ("ra_step", "ra_finalize", "ra_merge_lse", "ra_factored_spatial",
+EXPORTS = ("ra_step", "ra_finalize", "ra_step_final", "ra_merge_lse", "ra_factored_spatial",
            "ra_factored_temporal", "ra_kv_pass", "ra_status_string",
            "ra_last_hip_error", "ra_version")
 
@@ -46,6 +46,9 @@ _SIGS = {
                        ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
                        _vp, _vp, _vp, _vp]),
     "ra_finalize": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "ra_step_final": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                             ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
+                             _vp, _vp, _vp, _vp, _vp, _vp]),
     "ra_merge_lse": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "ra_factored_spatial": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                    _vp, _vp, _vp]),
@@ -127,6 +130,19 @@ def ra_step(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, init=False, st
                         RA_MASK_CAUSAL if causal else RA_MASK_NONE, float(scale),
                         RA_STEP_INIT if init else 0, _p(o_acc), _p(m), _p(l), _s(stream))
     _check("ra_step", st)
+
+
+def ra_step_final(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, out, lse=None,
+                  init=False, stream=None):
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    qs, ks = segs(q_segs), segs(kv_segs)
+    st = load().ra_step_final(_p(q), _p(k), _p(v), _dtype(q), B, H, Lq, Lk, d,
+                              ctypes.byref(qs), ctypes.byref(ks),
+                              RA_MASK_CAUSAL if causal else RA_MASK_NONE, float(scale),
+                              RA_STEP_INIT if init else 0, _p(o_acc), _p(m), _p(l), _p(out),
+                              _p(lse), _s(stream))
+    _check("ra_step_final", st)
 
 
 def ra_finalize(o_acc, m, l, out, lse=None, stream=None):

@@ -55,10 +55,13 @@ bool dims_ok(int32_t B, int32_t H, int32_t L) {
 
 extern "C" {
 
-ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B, int32_t H,
-                  int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
-                  const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
-                  float* o_acc, float* m, float* l, hipStream_t stream) {
+namespace {
+
+// Checks shared by ra_step and ra_step_final; fills the launch arguments.
+ra_status step_args(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B,
+                    int32_t H, int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
+                    const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
+                    float* o_acc, float* m, float* l, ra::StepArgs* out_args) {
   if (!q || !k || !v || !o_acc || !m || !l || !q_segs || !kv_segs) return RA_ERR_INVALID_ARG;
   if (!known_dtype(dt) || !dims_ok(B, H, Lq) || Lk <= 0 || d <= 0) return RA_ERR_INVALID_ARG;
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
@@ -83,7 +86,8 @@ ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt, int3
   // one (batch, head) slice of K or V must be addressable by a 32-bit offset
   if ((int64_t)Lk * d * (int64_t)es > (int64_t)INT32_MAX) return RA_ERR_UNSUPPORTED;
 
-  ra::StepArgs a{};
+  ra::StepArgs& a = *out_args;
+  a = ra::StepArgs{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -99,7 +103,47 @@ ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt, int3
   a.o_acc = o_acc;
   a.m = m;
   a.l = l;
+  return RA_OK;
+}
+
+}  // namespace
+
+ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B, int32_t H,
+                  int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
+                  const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
+                  float* o_acc, float* m, float* l, hipStream_t stream) {
+  ra::StepArgs a;
+  const ra_status st = step_args(q, k, v, dt, B, H, Lq, Lk, d, q_segs, kv_segs, mask, scale, flags,
+                                 o_acc, m, l, &a);
+  if (st != RA_OK) return st;
   return hip_fail(dt == RA_BF16 ? ra::launch_step_bf16(a, stream) : ra::launch_step_f32(a, stream));
+}
+
+ra_status ra_step_final(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B,
+                        int32_t H, int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
+                        const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
+                        float* o_acc, float* m, float* l, void* out, float* lse,
+                        hipStream_t stream) {
+  if (!out) return RA_ERR_INVALID_ARG;
+  ra::StepArgs a;
+  const ra_status st = step_args(q, k, v, dt, B, H, Lq, Lk, d, q_segs, kv_segs, mask, scale, flags,
+                                 o_acc, m, l, &a);
+  if (st != RA_OK) return st;
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4))) return RA_ERR_INVALID_ARG;
+  const size_t nb = (size_t)B * H, es = esize(dt), rows = nb * Lq;
+  const Range rout = span(out, rows * d * es);
+  const Range others[] = {span(q, rows * d * es), span(k, nb * Lk * d * es), span(v, nb * Lk * d * es),
+                          span(o_acc, rows * d * 4), span(m, rows * 4), span(l, rows * 4)};
+  for (Range x : others) {
+    if (overlap(rout, x)) return RA_ERR_INVALID_ARG;
+    if (lse && overlap(span(lse, rows * 4), x)) return RA_ERR_INVALID_ARG;
+  }
+  if (lse && overlap(span(lse, rows * 4), rout)) return RA_ERR_INVALID_ARG;
+  if (dt == RA_BF16) return hip_fail(ra::launch_step_last_bf16(a, out, lse, stream));
+  // fp32: the step, then the finalize of the updated state
+  const hipError_t e = ra::launch_step_f32(a, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return hip_fail(ra::launch_finalize(o_acc, m, l, (int64_t)rows, d, out, false, lse, stream));
 }
 
 ra_status ra_finalize(const float* o_acc, const float* m, const float* l, int32_t B, int32_t H,

@@ -28,6 +28,10 @@ struct StepArgs {
 };
 
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s);
+// The last ring step with the finalize folded in: out [nb, Lq, d] bf16 and
+// lse (may be null) from the state (read unless a.init) and the block; the
+// state is not written.
+hipError_t launch_step_last_bf16(const StepArgs& a, void* out, float* lse, hipStream_t s);
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t s);
 
 // Fused single-block attention (init + finalize): batched, unmasked, Lq = Lk.

@@ -120,7 +120,14 @@ struct Cursor {
   Item it;
 };
 
-template <int D, bool CAUSAL, bool FUSED>
+// What a launch reads and writes besides the queries and the block:
+//   kStep   running state in (unless init) and out;
+//   kAttend no state (a single block, init implied), final output out;
+//   kLast   running state in (unless init), final output out: the last ring
+//           step with the finalize folded in (the state is left unchanged).
+enum Mode { kStep = 0, kAttend = 1, kLast = 2 };
+
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, int32_t init,
@@ -132,6 +139,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   constexpr int NDMA = 2 * L::RUNS_PER_WAVE;  // load instructions per wave per tile
   __shared__ __attribute__((aligned(16))) char smem[kStages * L::STAGE];
 
+  constexpr bool FUSED = MODE != kStep;  // writes the final output
+  const bool state_in = MODE != kAttend && !init;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
 
@@ -192,14 +201,15 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
 
   // ---- items that see no key of the block keep their state: no loads and
   // no stores, except that a first step stores the empty state (and a fused
-  // call the empty output: zeros, lse -inf). NT counts the stream's tiles.
+  // call the empty output: zeros, lse -inf; a last step with a state in
+  // finalizes that state once the stream is done). NT counts the stream's tiles.
   int32_t NT = 0;
   for (int32_t i = 0; i < nrounds; ++i) {
     const int32_t lg = item_logical(i);
     if (lg < 0) continue;
     const Item it = decode(lg);
     NT += it.ntiles;
-    if (it.ntiles > 0 || (!FUSED && !init)) continue;
+    if (it.ntiles > 0 || state_in) continue;
     const int32_t qrow = it.qt0 + 32 * w + l32;
     if (qrow >= Lq) continue;
     const size_t r = (size_t)it.prob * Lq + qrow;
@@ -222,7 +232,36 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
       }
     }
   }
-  if (NT == 0) return;
+  // the output of the rows whose items see no key of a last block: the
+  // state they carry in, normalised (as the separate finalize does)
+  auto finalize_empty_items = [&]() RA_INLINE {
+    for (int32_t i = 0; i < nrounds; ++i) {
+      const int32_t lg = item_logical(i);
+      if (lg < 0) continue;
+      const Item it = decode(lg);
+      if (it.ntiles > 0) continue;
+      const int32_t qrow = it.qt0 + 32 * w + l32;
+      if (qrow >= Lq) continue;
+      const size_t r = (size_t)it.prob * Lq + qrow;
+      const float l = Lst[r];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float* ip = Oacc + r * D + 4 * h;
+      bf16* op = Out + r * D + 4 * h;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 x = *(const f32x4*)(ip + 32 * t + 8 * i4);
+          *(bf16x4*)(op + 32 * t + 8 * i4) =
+              bf16x4{to_bf16(x[0] * inv), to_bf16(x[1] * inv), to_bf16(x[2] * inv), to_bf16(x[3] * inv)};
+        }
+      if (Lse && h == 0) Lse[r] = l > 0.f ? Mst[r] + fast_log2(l) * kLn2 : kNegInf;
+    }
+  };
+  if (NT == 0) {
+    if (MODE == kLast && state_in) finalize_empty_items();
+    return;
+  }
 
   Cursor first;
   first.i = -1;
@@ -291,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     for (int t = 0; t < DT; ++t) o[t] = f32x16{};
     mu = kNegInf;
     lpart[0] = lpart[1] = 0.f;
-    if (!FUSED && !init && qvalid) {
+    if (state_in && qvalid) {
       const size_t r = (size_t)it.prob * Lq + qrow;
       const float* op = Oacc + r * D + 4 * h;
 #pragma unroll
@@ -620,6 +659,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     run(BoolC<true>{});
   else
     run(BoolC<false>{});
+  if (MODE == kLast && state_in) finalize_empty_items();
 }
 
 DevSegs dev(const HostSegs& s) { return DevSegs{s.start0, s.start1, s.len0, s.len}; }
@@ -638,14 +678,14 @@ int32_t cus_per_xcd() {
   return n;
 }
 
-template <int D, bool CAUSAL, bool FUSED>
+template <int D, bool CAUSAL, int MODE>
 hipError_t launch(const StepArgs& a, bf16* out, float* lse, hipStream_t st) {
   const int32_t nqt = (a.Lq + kBQ - 1) / kBQ;
   const int64_t total = (int64_t)a.nb * nqt;
   const int32_t per_xcd = (int32_t)((total + kXcds - 1) / kXcds);
   const int32_t nwg_x = min(per_xcd, cus_per_xcd());
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((step_mfma_kernel<D, CAUSAL, FUSED>), dim3(kXcds * nwg_x), dim3(kThreads), 0,
+  hipLaunchKernelGGL((step_mfma_kernel<D, CAUSAL, MODE>), dim3(kXcds * nwg_x), dim3(kThreads), 0,
                      st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.nb, a.Lq, a.Lk,
                      dev(a.qs), dev(a.ks), c, (int32_t)a.init, a.o_acc, a.m, a.l, out, lse, nqt,
                      per_xcd, nwg_x);
@@ -656,10 +696,17 @@ hipError_t launch(const StepArgs& a, bf16* out, float* lse, hipStream_t st) {
 
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t st) {
   if (a.d == 128)
-    return a.causal ? launch<128, true, false>(a, nullptr, nullptr, st)
-                    : launch<128, false, false>(a, nullptr, nullptr, st);
-  return a.causal ? launch<64, true, false>(a, nullptr, nullptr, st)
-                  : launch<64, false, false>(a, nullptr, nullptr, st);
+    return a.causal ? launch<128, true, kStep>(a, nullptr, nullptr, st)
+                    : launch<128, false, kStep>(a, nullptr, nullptr, st);
+  return a.causal ? launch<64, true, kStep>(a, nullptr, nullptr, st)
+                  : launch<64, false, kStep>(a, nullptr, nullptr, st);
+}
+
+hipError_t launch_step_last_bf16(const StepArgs& a, void* out, float* lse, hipStream_t st) {
+  bf16* o = (bf16*)out;
+  if (a.d == 128)
+    return a.causal ? launch<128, true, kLast>(a, o, lse, st) : launch<128, false, kLast>(a, o, lse, st);
+  return a.causal ? launch<64, true, kLast>(a, o, lse, st) : launch<64, false, kLast>(a, o, lse, st);
 }
 
 hipError_t launch_attend_bf16(const void* q, const void* k, const void* v, int32_t nb, int32_t L,
@@ -677,8 +724,8 @@ hipError_t launch_attend_bf16(const void* q, const void* k, const void* v, int32
   a.causal = false;
   a.init = true;
   a.scale = scale;
-  if (d == 128) return launch<128, false, true>(a, (bf16*)out, lse, st);
-  return launch<64, false, true>(a, (bf16*)out, lse, st);
+  if (d == 128) return launch<128, false, kAttend>(a, (bf16*)out, lse, st);
+  return launch<64, false, kAttend>(a, (bf16*)out, lse, st);
 }
 
 }  // namespace ra

@@ -7,8 +7,9 @@ folds it into the running state with ``ra_step``, and meanwhile the block for
 step s+1 is being passed to it. Here every rank's block already sits in this
 GPU's memory, so the pass is ``ra_kv_pass`` (a device-to-device copy) enqueued
 on a side stream into one half of a double buffer, ordered against the compute
-stream with events exactly as a network receive would be. After the last step
-``ra_finalize`` writes the output and its log-sum-exp.
+stream with events exactly as a network receive would be. The last step is
+``ra_step_final``: the same kernel folds in the last block and writes the
+output and its log-sum-exp (no separate finalize pass over the state).
 
 This module is host control only: every byte of the path moves in libra.
 """
@@ -53,6 +54,9 @@ def run(q: torch.Tensor,
     order      source rank per step (default: the ring, (rank - s) mod P)
     prefetch   True: pass the next block on `copy_stream` while the current
                step computes; False: pass it on the compute stream first
+    finalize   True: the last step writes out and lse (the state is then left
+               as it was before the last block); False: every step updates the
+               state and out / lse are not written
     returns (out [B, H, Lq, d] in q's dtype, lse [B, H, Lq] fp32, state)
     """
     P = len(kv_blocks)
@@ -114,13 +118,19 @@ def run(q: torch.Tensor,
             k, v = kv_blocks[order[s]]
         if step_events is not None:
             step_events[s][0].record(compute)
-        _lib.ra_step(q, k, v, q_segs, kv_segs[order[s]], causal, scale,
-                     state.o, state.m, state.l, init=(s == 0), stream=compute)
+        if finalize and s == P - 1:
+            # the last block: the output is written straight from the kernel
+            # (the state is left as the previous steps wrote it)
+            _lib.ra_step_final(q, k, v, q_segs, kv_segs[order[s]], causal, scale,
+                               state.o, state.m, state.l, out, lse, init=(s == 0), stream=compute)
+        else:
+            _lib.ra_step(q, k, v, q_segs, kv_segs[order[s]], causal, scale,
+                         state.o, state.m, state.l, init=(s == 0), stream=compute)
         if step_events is not None:
             step_events[s][1].record(compute)
-        if needs_pass[s]:
+        # the slot is free again after this step; only a later block passed
+        # into the same slot waits for that (an event record costs a queue packet)
+        if prefetch and needs_pass[s] and any(needs_pass[s + 2::2]):
             ev_free[s % 2].record(compute)
             used[s % 2] = True
-    if finalize:
-        _lib.ra_finalize(state.o, state.m, state.l, out, lse, stream=compute)
     return out, lse, state

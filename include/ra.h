@@ -127,6 +127,28 @@ ra_status ra_finalize(const float* o_acc, const float* m, const float* l,
                       void* out, ra_dtype out_dt, float* lse, hipStream_t stream);
 
 /*
+ * ra_step_final — the last ring step with the finalize folded in: the result
+ * of ra_step on this block followed by ra_finalize (Day 83 post, "Context
+ * parallelism: splitting the sequence": after the last block the device
+ * holds the exact output of its queries).
+ * Arguments as for ra_step, plus
+ *   out  [B,H,Lq,d] of dt: (o_acc' / l') with the state after this block;
+ *   lse  [B,H,Lq] fp32 (m' + ln l'), or NULL.
+ * A row with no visible key in any block gets out = 0 and lse = -inf.
+ * The state (o_acc, m, l) is an input (not read with RA_STEP_INIT); its
+ * contents afterwards are unspecified (the bf16 path leaves it unchanged and
+ * never writes the updated state: the output is written straight from the
+ * registers; the fp32 path runs the step and the finalize).
+ * Errors: those of ra_step, and RA_ERR_INVALID_ARG for a null out or out /
+ *   lse overlapping the inputs or the state.
+ */
+ra_status ra_step_final(const void* q, const void* k, const void* v, ra_dtype dt,
+                        int32_t B, int32_t H, int32_t Lq, int32_t Lk, int32_t d,
+                        const ra_segs* q_segs, const ra_segs* kv_segs, ra_mask mask,
+                        float scale, uint32_t flags, float* o_acc, float* m, float* l,
+                        void* out, float* lse, hipStream_t stream);
+
+/*
  * ra_merge_lse — combine two normalised partial attentions of the same queries
  * over disjoint key sets (the partial outputs the Day 83 post's devices
  * accumulate, "Context parallelism: splitting the sequence"):

@@ -210,6 +210,51 @@ def test_block_after_every_query_leaves_state_untouched(gpu_lib):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d,dt", [(128, torch.bfloat16), (64, torch.bfloat16), (64, torch.float32)])
+@pytest.mark.parametrize("init", [False, True])
+def test_step_final_equals_step_then_finalize(gpu_lib, d, dt, init):
+    banner(f"ra_step_final vs ra_step + ra_finalize: d{d} {dt} init={init}")
+    B, H, L, Lk = 1, 3, 700, 300
+    q = seeded.gen_bhsd(83, 0, B, H, 0, L, d, dt, "cuda")
+    ka = seeded.gen_bhsd(83, 1, B, H, 0, L, d, dt, "cuda")
+    va = seeded.gen_bhsd(83, 2, B, H, 0, L, d, dt, "cuda")
+    kb = seeded.gen_bhsd(83, 3, B, H, 0, Lk, d, dt, "cuda")
+    vb = seeded.gen_bhsd(83, 4, B, H, 0, Lk, d, dt, "cuda")
+    scale = d ** -0.5
+    qr = [(0, L)]
+    # block b at positions 600..899: the query rows before 600 (the first two
+    # 256-row tiles) see none of it, the third tile straddles the diagonal
+    kbr = [(600, Lk)]
+    st = ring.RingState(B, H, L, d, "cuda")
+    if not init:
+        _lib.ra_step(q, ka, va, qr, [(0, L)], True, scale, st.o, st.m, st.l, init=True)
+    before = (st.o.clone(), st.m.clone(), st.l.clone())
+    out2 = torch.empty_like(q)
+    lse2 = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    _lib.ra_step_final(q, kb, vb, qr, kbr, True, scale, st.o, st.m, st.l, out2, lse2, init=init)
+    torch.cuda.synchronize()
+    if dt == torch.bfloat16:
+        # the state is an input only on the matrix-core path
+        for a, b in zip(before, (st.o, st.m, st.l)):
+            assert torch.equal(a, b)
+    ref = ring.RingState(B, H, L, d, "cuda")
+    for x, y in zip((ref.o, ref.m, ref.l), before):
+        x.copy_(y)
+    _lib.ra_step(q, kb, vb, qr, kbr, True, scale, ref.o, ref.m, ref.l, init=init)
+    out1 = torch.empty_like(q)
+    lse1 = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    _lib.ra_finalize(ref.o, ref.m, ref.l, out1, lse1)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(torch.isneginf(lse1), torch.isneginf(lse2))
+    fin = torch.isfinite(lse1)
+    assert torch.all(torch.isfinite(lse2) == fin)
+    assert (lse1[fin] - lse2[fin]).abs().max().item() <= 1e-5
+    if init:
+        # rows before position 600 see no key at all
+        assert torch.all(out2[:, :, :600].float() == 0) and torch.all(torch.isneginf(lse2[:, :, :600]))
+
+
 # ---- invariants on the GPU --------------------------------------------------------
 
 @pytest.fixture(scope="module")
