@@ -49,10 +49,10 @@ def make_ring_inputs(w, rank, dev):
     segs = [layout.split(w.split, w.S, w.P, t, S_sp=w.S_sp) for t in range(w.P)]
     pos = [torch.as_tensor(positions(s), device=dev) for s in segs]
     q = seeded.gen_bhsd_at(w.wid, seeded.Q, w.B, w.H, positions(segs[rank]), w.d, w.dtype, dev)
-    kv = [(torch.empty((w.B, w.H, w.L, w.d), dtype=w.dtype, device=dev),
-           torch.empty((w.B, w.H, w.L, w.d), dtype=w.dtype, device=dev)) for _ in range(w.P)]
+    kv = [(torch.empty((w.B, w.Hkv, w.L, w.d), dtype=w.dtype, device=dev),
+           torch.empty((w.B, w.Hkv, w.L, w.d), dtype=w.dtype, device=dev)) for _ in range(w.P)]
     for b in range(w.B):
-        for h in range(w.H):
+        for h in range(w.Hkv):
             for tid, slot in ((seeded.K, 0), (seeded.V, 1)):
                 g = seeded.to_dtype(seeded.normal_rows(w.wid, tid, b, h, 0, w.S, w.d), w.dtype).to(dev)
                 for t in range(w.P):
@@ -207,9 +207,10 @@ def cpu_baseline(w, rank, segs, budget_s):
     while elapsed < budget_s:
         h = i % (w.B * w.H)
         b, hh = divmod(h, w.H)
-        if h not in kv:  # one head's global K and V, kept for later runs of that head
+        if h not in kv:  # the global K and V this head reads, kept for later runs of that head
+            hk = hh // (w.H // w.Hkv)  # consecutive query heads share a K/V head
             kv[h] = tuple(seeded.exact_f64(seeded.to_dtype(
-                seeded.normal_rows(w.wid, t, b, hh, 0, w.S, w.d), w.dtype)) for t in (seeded.K, seeded.V))
+                seeded.normal_rows(w.wid, t, b, hk, 0, w.S, w.d), w.dtype)) for t in (seeded.K, seeded.V))
         kf, vf = kv[h]
         r0 = int(rng.integers(0, max(1, qpos_all.size - chunk)))
         qp = qpos_all[r0:r0 + chunk]
@@ -295,7 +296,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
         "data": "synthetic (seeded N(0,1), rounded to bf16)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "global_seq": w.S,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "d": w.d, "global_seq": w.S,
                    "ring_P": w.P, "rank": args.rank, "local_q": w.L, "split": w.split,
                    "causal": w.causal, "prefetch": not args.no_prefetch,
                    "parallelism": "one rank's share, ring simulated on 1 GPU"},

@@ -21,7 +21,8 @@ RA_MASK_NONE, RA_MASK_CAUSAL = 0, 1
 RA_STEP_INIT = 1
 
 # every symbol include/ra.h declares
-EXPORTS = ("ra_step", "ra_finalize", "ra_step_final", "ra_merge_lse", "ra_factored_spatial",
+EXPORTS = ("ra_step", "ra_finalize", "ra_step_final", "ra_step_gqa", "ra_step_final_gqa",
+           "ra_merge_lse", "ra_factored_spatial",
            "ra_factored_temporal", "ra_kv_pass", "ra_status_string",
            "ra_last_hip_error", "ra_version")
 
@@ -45,6 +46,12 @@ _SIGS = {
     "ra_step": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                        ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
                        _vp, _vp, _vp, _vp]),
+    "ra_step_gqa": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                           ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
+                           _vp, _vp, _vp, _vp]),
+    "ra_step_final_gqa": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
+                                 _vp, _vp, _vp, _vp, _vp, _vp]),
     "ra_finalize": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "ra_step_final": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                              ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
@@ -122,27 +129,34 @@ def _s(stream) -> Optional[int]:
 
 
 def ra_step(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, init=False, stream=None):
+    """ra_step; with fewer K/V heads than query heads (k.shape[1] < q.shape[1]) ra_step_gqa."""
     B, H, Lq, d = q.shape
-    Lk = k.shape[2]
+    H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
-    st = load().ra_step(_p(q), _p(k), _p(v), _dtype(q), B, H, Lq, Lk, d,
-                        ctypes.byref(qs), ctypes.byref(ks),
-                        RA_MASK_CAUSAL if causal else RA_MASK_NONE, float(scale),
-                        RA_STEP_INIT if init else 0, _p(o_acc), _p(m), _p(l), _s(stream))
-    _check("ra_step", st)
+    args = (ctypes.byref(qs), ctypes.byref(ks), RA_MASK_CAUSAL if causal else RA_MASK_NONE,
+            float(scale), RA_STEP_INIT if init else 0, _p(o_acc), _p(m), _p(l), _s(stream))
+    if H_kv == H:
+        _check("ra_step", load().ra_step(_p(q), _p(k), _p(v), _dtype(q), B, H, Lq, Lk, d, *args))
+    else:
+        _check("ra_step_gqa", load().ra_step_gqa(_p(q), _p(k), _p(v), _dtype(q), B, H, H_kv, Lq,
+                                                 Lk, d, *args))
 
 
 def ra_step_final(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, out, lse=None,
                   init=False, stream=None):
+    """ra_step_final; with fewer K/V heads than query heads ra_step_final_gqa."""
     B, H, Lq, d = q.shape
-    Lk = k.shape[2]
+    H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
-    st = load().ra_step_final(_p(q), _p(k), _p(v), _dtype(q), B, H, Lq, Lk, d,
-                              ctypes.byref(qs), ctypes.byref(ks),
-                              RA_MASK_CAUSAL if causal else RA_MASK_NONE, float(scale),
-                              RA_STEP_INIT if init else 0, _p(o_acc), _p(m), _p(l), _p(out),
-                              _p(lse), _s(stream))
-    _check("ra_step_final", st)
+    args = (ctypes.byref(qs), ctypes.byref(ks), RA_MASK_CAUSAL if causal else RA_MASK_NONE,
+            float(scale), RA_STEP_INIT if init else 0, _p(o_acc), _p(m), _p(l), _p(out),
+            _p(lse), _s(stream))
+    if H_kv == H:
+        _check("ra_step_final", load().ra_step_final(_p(q), _p(k), _p(v), _dtype(q), B, H, Lq,
+                                                     Lk, d, *args))
+    else:
+        _check("ra_step_final_gqa", load().ra_step_final_gqa(_p(q), _p(k), _p(v), _dtype(q), B, H,
+                                                             H_kv, Lq, Lk, d, *args))
 
 
 def ra_finalize(o_acc, m, l, out, lse=None, stream=None):

@@ -1,4 +1,4 @@
-"""The five synthetic workloads, by name.
+"""The synthetic workloads, by name.
 
 Each ring workload describes one rank's share: the global sequence S, the ring
 size P, the split that decides which global positions the rank holds, the mask
@@ -26,10 +26,15 @@ class RingWorkload:
     dtype: torch.dtype
     S_sp: int = 0       # spatial tokens per frame (temporal split only)
     sample_rows: Optional[int] = None  # rows the oracle checks (None = all)
+    H_kv: int = 0       # K/V heads (0: one per query head); H % H_kv == 0
 
     @property
     def L(self) -> int:
         return self.S // self.P
+
+    @property
+    def Hkv(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def scale(self) -> float:
@@ -75,5 +80,15 @@ VIDEO_DIT_CP8 = RingWorkload(5, "video-dit-432k-cp8", B=1, H=32, d=128, S=432000
                              split="temporal", causal=False, dtype=torch.bfloat16,
                              S_sp=3600, sample_rows=4096)
 
-RING_WORKLOADS = {w.name: w for w in (TINY_F32, CAUSAL_2RANK, LLM_32K_CP4, VIDEO_DIT_CP8)}
+# Grouped K/V heads (fewer K/V heads than query heads; the k8ai page ties the
+# ring's bytes per step to the K/V head count): the causal 4K share with 8
+# query heads over 2 K/V heads, and the 32K share with 32 over 8.
+CAUSAL_2RANK_GQA = RingWorkload(6, "causal-bf16-4k-cp2-gqa4", B=1, H=8, d=64, S=4096, P=2,
+                                split="zigzag", causal=True, dtype=torch.bfloat16, H_kv=2)
+LLM_32K_CP4_GQA = RingWorkload(7, "llm-32k-causal-cp4-gqa4", B=1, H=32, d=128, S=32768, P=4,
+                               split="zigzag", causal=True, dtype=torch.bfloat16,
+                               sample_rows=4096, H_kv=8)
+
+RING_WORKLOADS = {w.name: w for w in (TINY_F32, CAUSAL_2RANK, LLM_32K_CP4, VIDEO_DIT_CP8,
+                                      CAUSAL_2RANK_GQA, LLM_32K_CP4_GQA)}
 ALL = {**RING_WORKLOADS, VIDEO_FACTORED.name: VIDEO_FACTORED}

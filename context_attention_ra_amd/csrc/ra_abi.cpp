@@ -59,11 +59,12 @@ namespace {
 
 // Checks shared by ra_step and ra_step_final; fills the launch arguments.
 ra_status step_args(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B,
-                    int32_t H, int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
-                    const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
-                    float* o_acc, float* m, float* l, ra::StepArgs* out_args) {
+                    int32_t H, int32_t H_kv, int32_t Lq, int32_t Lk, int32_t d,
+                    const ra_segs* q_segs, const ra_segs* kv_segs, ra_mask mask, float scale,
+                    uint32_t flags, float* o_acc, float* m, float* l, ra::StepArgs* out_args) {
   if (!q || !k || !v || !o_acc || !m || !l || !q_segs || !kv_segs) return RA_ERR_INVALID_ARG;
   if (!known_dtype(dt) || !dims_ok(B, H, Lq) || Lk <= 0 || d <= 0) return RA_ERR_INVALID_ARG;
+  if (H_kv <= 0 || H % H_kv != 0) return RA_ERR_INVALID_ARG;
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return RA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return RA_ERR_INVALID_ARG;
   if (flags & ~RA_STEP_INIT) return RA_ERR_INVALID_ARG;
@@ -72,9 +73,9 @@ ra_status step_args(const void* q, const void* k, const void* v, ra_dtype dt, in
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_acc, 16) ||
       !aligned(m, 4) || !aligned(l, 4))
     return RA_ERR_INVALID_ARG;
-  const size_t nb = (size_t)B * H, es = esize(dt);
-  const Range rq = span(q, nb * Lq * d * es), rk = span(k, nb * Lk * d * es),
-              rv = span(v, nb * Lk * d * es), ro = span(o_acc, nb * Lq * d * 4),
+  const size_t nb = (size_t)B * H, nkv = (size_t)B * H_kv, es = esize(dt);
+  const Range rq = span(q, nb * Lq * d * es), rk = span(k, nkv * Lk * d * es),
+              rv = span(v, nkv * Lk * d * es), ro = span(o_acc, nb * Lq * d * 4),
               rm = span(m, nb * Lq * 4), rl = span(l, nb * Lq * 4);
   for (Range st : {ro, rm, rl})
     for (Range in : {rq, rk, rv})
@@ -95,6 +96,7 @@ ra_status step_args(const void* q, const void* k, const void* v, ra_dtype dt, in
   a.Lq = Lq;
   a.Lk = Lk;
   a.d = d;
+  a.group = H / H_kv;
   a.qs = qs;
   a.ks = ks;
   a.causal = mask == RA_MASK_CAUSAL;
@@ -108,31 +110,39 @@ ra_status step_args(const void* q, const void* k, const void* v, ra_dtype dt, in
 
 }  // namespace
 
-ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B, int32_t H,
-                  int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
-                  const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
-                  float* o_acc, float* m, float* l, hipStream_t stream) {
+ra_status ra_step_gqa(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B,
+                      int32_t H, int32_t H_kv, int32_t Lq, int32_t Lk, int32_t d,
+                      const ra_segs* q_segs, const ra_segs* kv_segs, ra_mask mask, float scale,
+                      uint32_t flags, float* o_acc, float* m, float* l, hipStream_t stream) {
   ra::StepArgs a;
-  const ra_status st = step_args(q, k, v, dt, B, H, Lq, Lk, d, q_segs, kv_segs, mask, scale, flags,
-                                 o_acc, m, l, &a);
+  const ra_status st = step_args(q, k, v, dt, B, H, H_kv, Lq, Lk, d, q_segs, kv_segs, mask, scale,
+                                 flags, o_acc, m, l, &a);
   if (st != RA_OK) return st;
   return hip_fail(dt == RA_BF16 ? ra::launch_step_bf16(a, stream) : ra::launch_step_f32(a, stream));
 }
 
-ra_status ra_step_final(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B,
-                        int32_t H, int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
-                        const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
-                        float* o_acc, float* m, float* l, void* out, float* lse,
-                        hipStream_t stream) {
+ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B, int32_t H,
+                  int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
+                  const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
+                  float* o_acc, float* m, float* l, hipStream_t stream) {
+  return ra_step_gqa(q, k, v, dt, B, H, H, Lq, Lk, d, q_segs, kv_segs, mask, scale, flags, o_acc,
+                     m, l, stream);
+}
+
+ra_status ra_step_final_gqa(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B,
+                            int32_t H, int32_t H_kv, int32_t Lq, int32_t Lk, int32_t d,
+                            const ra_segs* q_segs, const ra_segs* kv_segs, ra_mask mask,
+                            float scale, uint32_t flags, float* o_acc, float* m, float* l,
+                            void* out, float* lse, hipStream_t stream) {
   if (!out) return RA_ERR_INVALID_ARG;
   ra::StepArgs a;
-  const ra_status st = step_args(q, k, v, dt, B, H, Lq, Lk, d, q_segs, kv_segs, mask, scale, flags,
-                                 o_acc, m, l, &a);
+  const ra_status st = step_args(q, k, v, dt, B, H, H_kv, Lq, Lk, d, q_segs, kv_segs, mask, scale,
+                                 flags, o_acc, m, l, &a);
   if (st != RA_OK) return st;
   if (!aligned(out, 16) || (lse && !aligned(lse, 4))) return RA_ERR_INVALID_ARG;
-  const size_t nb = (size_t)B * H, es = esize(dt), rows = nb * Lq;
+  const size_t nb = (size_t)B * H, nkv = (size_t)B * H_kv, es = esize(dt), rows = nb * Lq;
   const Range rout = span(out, rows * d * es);
-  const Range others[] = {span(q, rows * d * es), span(k, nb * Lk * d * es), span(v, nb * Lk * d * es),
+  const Range others[] = {span(q, rows * d * es), span(k, nkv * Lk * d * es), span(v, nkv * Lk * d * es),
                           span(o_acc, rows * d * 4), span(m, rows * 4), span(l, rows * 4)};
   for (Range x : others) {
     if (overlap(rout, x)) return RA_ERR_INVALID_ARG;
@@ -144,6 +154,15 @@ ra_status ra_step_final(const void* q, const void* k, const void* v, ra_dtype dt
   const hipError_t e = ra::launch_step_f32(a, stream);
   if (e != hipSuccess) return hip_fail(e);
   return hip_fail(ra::launch_finalize(o_acc, m, l, (int64_t)rows, d, out, false, lse, stream));
+}
+
+ra_status ra_step_final(const void* q, const void* k, const void* v, ra_dtype dt, int32_t B,
+                        int32_t H, int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
+                        const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
+                        float* o_acc, float* m, float* l, void* out, float* lse,
+                        hipStream_t stream) {
+  return ra_step_final_gqa(q, k, v, dt, B, H, H, Lq, Lk, d, q_segs, kv_segs, mask, scale, flags,
+                           o_acc, m, l, out, lse, stream);
 }
 
 ra_status ra_finalize(const float* o_acc, const float* m, const float* l, int32_t B, int32_t H,
@@ -257,6 +276,6 @@ const char* ra_status_string(ra_status s) {
 
 int32_t ra_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t ra_version(void) { return 100; }
+int32_t ra_version(void) { return 200; }
 
 }  // extern "C"

@@ -11,13 +11,15 @@ struct HostSegs {
   int32_t start0, start1, len0, len;
 };
 
-// One problem of the step kernels: `nb` independent (batch*head) slices, each
-// with Lq query rows and Lk key rows.
+// One problem of the step kernels: `nb` independent (batch*head) query slices,
+// each with Lq query rows, against nb / group K/V slices of Lk key rows:
+// query slice p reads K/V slice p / group.
 struct StepArgs {
   const void* q;
   const void* k;
   const void* v;
   int32_t nb, Lq, Lk, d;
+  int32_t group;  // query heads per K/V head (1: one K/V head per query head)
   HostSegs qs, ks;
   bool causal;
   bool init;

@@ -20,7 +20,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void step_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, int32_t init,
-    float* __restrict__ Oacc, float* __restrict__ Mst, float* __restrict__ Lst, int32_t nqt) {
+    float* __restrict__ Oacc, float* __restrict__ Mst, float* __restrict__ Lst, int32_t nqt,
+    int32_t group) {
   constexpr int TPR = D / 32;                 // lanes per query row
   constexpr int RPB = kThreads / TPR;         // query rows per workgroup
   __shared__ f32x4 kt[kBK * D / 4];
@@ -35,7 +36,8 @@ __global__ __launch_bounds__(kThreads) void step_f32_kernel(
   const int32_t qrow_c = qvalid ? qrow : Lq - 1;
   const int32_t qpos = seg_pos(qs, qrow_c);
   const size_t qoff = ((size_t)prob * Lq + qrow_c) * D + 32 * part;
-  const size_t kbase = (size_t)prob * Lk * D;
+  // query heads h*group .. h*group+group-1 share K/V head h (batch-major slices)
+  const size_t kbase = (size_t)(prob / group) * Lk * D;
 
   float q[32], o[32];
 #pragma unroll
@@ -146,7 +148,7 @@ hipError_t launch(const StepArgs& a, hipStream_t st) {
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, a.Lq, a.Lk,
                      DevSegs{a.qs.start0, a.qs.start1, a.qs.len0, a.qs.len},
                      DevSegs{a.ks.start0, a.ks.start1, a.ks.len0, a.ks.len}, a.scale * kLog2e,
-                     (int32_t)a.init, a.o_acc, a.m, a.l, nqt);
+                     (int32_t)a.init, a.o_acc, a.m, a.l, nqt, a.group);
   return hipGetLastError();
 }
 

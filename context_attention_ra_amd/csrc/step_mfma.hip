@@ -107,10 +107,11 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-// One work item: query tile qt0.. of slice prob, and the K/V tiles it sees
-// (two runs of tile indices: t0a.. (n0 tiles) and t1a.. (the rest)).
+// One work item: query tile qt0.. of slice prob, the K/V slice kvp it reads,
+// and the K/V tiles it sees (two runs of tile indices: t0a.. (n0 tiles) and
+// t1a.. (the rest)).
 struct Item {
-  int32_t prob, qt0, n0, t0a, t1a, ntiles;
+  int32_t prob, kvp, qt0, n0, t0a, t1a, ntiles;
 };
 
 // A position in a workgroup's stream of tiles: item number i of the
@@ -132,7 +133,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, int32_t init,
     float* __restrict__ Oacc, float* __restrict__ Mst, float* __restrict__ Lst,
-    bf16* __restrict__ Out, float* __restrict__ Lse, int32_t nqt, int32_t per_xcd, int32_t nwg_x) {
+    bf16* __restrict__ Out, float* __restrict__ Lse, int32_t nqt, int32_t per_xcd, int32_t nwg_x,
+    int32_t group) {
   using L = Lay<D>;
   constexpr int KS = D / 16;  // k-steps of the score MFMA
   constexpr int DT = D / 32;  // 32-wide output tiles
@@ -158,6 +160,9 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   auto decode = [&](int32_t logical) RA_INLINE {
     Item it;
     it.prob = logical / nqt;
+    // query heads h*group .. h*group+group-1 of a batch share K/V head h;
+    // slices are batch-major, so the K/V slice is the query slice / group
+    it.kvp = it.prob / group;
     const int32_t qtile = nqt - 1 - (logical - it.prob * nqt);
     it.qt0 = qtile * kBQ;
     // key rows this item can see: at most two row ranges
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   int32_t fg = 0;     // stream index of the next tile to request
   auto fetch_next = [&]() RA_INLINE {
     if (fg == fc.g1) advance(fc);
-    const size_t kbase = (size_t)fc.it.prob * Lk * D;
+    const size_t kbase = (size_t)fc.it.kvp * Lk * D;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(K + kbase), 0, Lk * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
@@ -688,7 +693,7 @@ hipError_t launch(const StepArgs& a, bf16* out, float* lse, hipStream_t st) {
   hipLaunchKernelGGL((step_mfma_kernel<D, CAUSAL, MODE>), dim3(kXcds * nwg_x), dim3(kThreads), 0,
                      st, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.nb, a.Lq, a.Lk,
                      dev(a.qs), dev(a.ks), c, (int32_t)a.init, a.o_acc, a.m, a.l, out, lse, nqt,
-                     per_xcd, nwg_x);
+                     per_xcd, nwg_x, a.group);
   return hipGetLastError();
 }
 
@@ -721,6 +726,7 @@ hipError_t launch_attend_bf16(const void* q, const void* k, const void* v, int32
   a.d = d;
   a.qs = HostSegs{0, 0, L, L};
   a.ks = HostSegs{0, 0, L, L};
+  a.group = 1;
   a.causal = false;
   a.init = true;
   a.scale = scale;

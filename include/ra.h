@@ -149,6 +149,32 @@ ra_status ra_step_final(const void* q, const void* k, const void* v, ra_dtype dt
                         void* out, float* lse, hipStream_t stream);
 
 /*
+ * ra_step_gqa, ra_step_final_gqa — ra_step and ra_step_final with fewer K/V
+ * heads than query heads. The k8ai page ("Communication profile") notes that
+ * the bytes a ring moves per step grow with the number of K/V heads, so a
+ * model that shares each K/V head among several query heads passes
+ * proportionally smaller blocks.
+ * H_kv  K/V heads, 1 <= H_kv <= H and H % H_kv == 0. Query head h of batch b
+ *       attends to K/V head h / (H / H_kv) of batch b (consecutive query heads
+ *       form a group).
+ * k, v  [B,H_kv,Lk,d]; every other argument, the state and the result are as
+ *       for ra_step / ra_step_final (q, o_acc, m, l, out, lse have H heads).
+ * With H_kv == H these are exactly ra_step and ra_step_final.
+ * Errors: those of ra_step / ra_step_final, and RA_ERR_INVALID_ARG for
+ *   H_kv <= 0 or H not a multiple of H_kv.
+ */
+ra_status ra_step_gqa(const void* q, const void* k, const void* v, ra_dtype dt,
+                      int32_t B, int32_t H, int32_t H_kv, int32_t Lq, int32_t Lk, int32_t d,
+                      const ra_segs* q_segs, const ra_segs* kv_segs, ra_mask mask,
+                      float scale, uint32_t flags, float* o_acc, float* m, float* l,
+                      hipStream_t stream);
+ra_status ra_step_final_gqa(const void* q, const void* k, const void* v, ra_dtype dt,
+                            int32_t B, int32_t H, int32_t H_kv, int32_t Lq, int32_t Lk,
+                            int32_t d, const ra_segs* q_segs, const ra_segs* kv_segs,
+                            ra_mask mask, float scale, uint32_t flags, float* o_acc,
+                            float* m, float* l, void* out, float* lse, hipStream_t stream);
+
+/*
  * ra_merge_lse — combine two normalised partial attentions of the same queries
  * over disjoint key sets (the partial outputs the Day 83 post's devices
  * accumulate, "Context parallelism: splitting the sequence"):

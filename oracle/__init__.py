@@ -17,13 +17,15 @@ Sources (cited by page title and section):
 * Ultralytics glossary, "Context Parallelism": "How Context Parallelism Works",
   "Practical Use and Tradeoffs".
 * k8ai concepts, "Sequence and Context Parallel": "How context parallel works"
-  (the ring figure and the causal balance remark).
+  (the ring figure and the causal balance remark), "Communication profile"
+  (ring volume and the number of K/V heads).
 """
 
 from .attention import (  # noqa: F401
     attention_rows,
     factored_spatial,
     factored_temporal,
+    grouped_attention,
     merge_lse,
 )
 from .layout import (  # noqa: F401

@@ -69,6 +69,33 @@ def attention_rows(q, q_pos, k, v, k_pos, scale, causal, row_chunk=256):
     return o, lse
 
 
+def grouped_attention(q, q_pos, k, v, k_pos, scale, causal):
+    """Attention of H query heads when groups of query heads share a K/V head.
+
+    The k8ai page ("Communication profile") ties the bytes a ring moves per
+    step to the number of K/V heads; a model with fewer K/V heads than query
+    heads lets each K/V head serve a group of query heads. The pages do not
+    say which query heads form a group; the reading taken here is consecutive
+    groups: with G = H / H_kv, query head h attends to K/V head floor(h / G).
+    Each head is then the plain attention of ``attention_rows``.
+
+    q      (H, n, d)     query rows of every head
+    k, v   (H_kv, S, d)  keys and values of every K/V head, H % H_kv == 0
+    other arguments as ``attention_rows``
+    returns (o (H, n, d) fp64, lse (H, n) fp64)
+    """
+    H, n, d = np.shape(q)
+    H_kv = np.shape(k)[0]
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError("the query head count must be a multiple of the K/V head count")
+    G = H // H_kv
+    o = np.zeros((H, n, np.shape(v)[2]), dtype=np.float64)
+    lse = np.zeros((H, n), dtype=np.float64)
+    for h in range(H):
+        o[h], lse[h] = attention_rows(q[h], q_pos, k[h // G], v[h // G], k_pos, scale, causal)
+    return o, lse
+
+
 def factored_spatial(q, k, v, T, S_sp, scale):
     """Spatial attention of a frame-major video token sequence.
 

@@ -30,17 +30,17 @@ class RingCase:
 
     def __init__(self, w, rank, device="cuda"):
         self.w, self.rank = w, rank
-        B, H, d, P = w.B, w.H, w.d, w.P
+        B, H, Hkv, d, P = w.B, w.H, w.Hkv, w.d, w.P
         self.q_segs = pkg_segs(w, rank)
         self.kv_segs = [pkg_segs(w, t) for t in range(P)]
         qpos = oracle_positions(w, rank)
         self.q = seeded.gen_bhsd_at(w.wid, seeded.Q, B, H, qpos, d, w.dtype, device)
         L = w.L
-        self.kv = [(torch.empty((B, H, L, d), dtype=w.dtype, device=device),
-                    torch.empty((B, H, L, d), dtype=w.dtype, device=device)) for _ in range(P)]
+        self.kv = [(torch.empty((B, Hkv, L, d), dtype=w.dtype, device=device),
+                    torch.empty((B, Hkv, L, d), dtype=w.dtype, device=device)) for _ in range(P)]
         pos_t = [torch.as_tensor(oracle_positions(w, t), device=device) for t in range(P)]
         for b in range(B):
-            for h in range(H):
+            for h in range(Hkv):
                 for tid, slot in ((seeded.K, 0), (seeded.V, 1)):
                     g = seeded.to_dtype(seeded.normal_rows(w.wid, tid, b, h, 0, w.S, d), w.dtype).to(device)
                     for t in range(P):
@@ -54,6 +54,16 @@ class RingCase:
         qpos = qpos_all[rows]
         o = np.zeros((w.B, w.H, rows.size, w.d))
         lse = np.zeros((w.B, w.H, rows.size))
+        ex = lambda tid, b, h, r: seeded.exact_f64(seeded.to_dtype(
+            seeded.normal_rows_at(w.wid, tid, b, h, r, w.d), w.dtype))
+        if w.Hkv != w.H:
+            # grouped K/V heads: the oracle decides which K/V head a query head reads
+            for b in range(w.B):
+                q = np.stack([ex(seeded.Q, b, h, qpos) for h in range(w.H)])
+                k = np.stack([ex(seeded.K, b, h, np.arange(w.S)) for h in range(w.Hkv)])
+                v = np.stack([ex(seeded.V, b, h, np.arange(w.S)) for h in range(w.Hkv)])
+                o[b], lse[b] = oracle.grouped_attention(q, qpos, k, v, np.arange(w.S), w.scale, w.causal)
+            return o, lse
         for b in range(w.B):
             for h in range(w.H):
                 q = seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, seeded.Q, b, h, qpos, w.d), w.dtype))

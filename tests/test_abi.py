@@ -130,3 +130,40 @@ def test_kv_pass_validation(lib):
     assert lib.ra_kv_pass(None, ptr(1), ptr(2), ptr(3), 64, None) == INV
     assert lib.ra_kv_pass(ptr(0), ptr(1), ptr(0), ptr(3), 64, None) == INV
     assert lib.ra_kv_pass(ptr(0), ptr(1), ptr(2), ptr(2) + 32, 64, None) == INV
+
+
+def step_gqa(lib, H=4, H_kv=2, d=128, final=False, out=None):
+    a, b = _lib.segs([(0, 64)]), _lib.segs([(0, 64)])
+    args = (ptr(0), ptr(1), ptr(2), 1, 1, H, H_kv, 64, 64, d, ctypes.byref(a), ctypes.byref(b), 1,
+            0.1, 1, ptr(3), ptr(4), ptr(5))
+    if final:
+        return lib.ra_step_final_gqa(*args, out, None, None)
+    return lib.ra_step_gqa(*args, None)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 0), (4, -2), (6, 4), (4, 8), (3, 2)])
+def test_gqa_rejects_heads_that_do_not_divide(lib, H, H_kv):
+    assert step_gqa(lib, H=H, H_kv=H_kv) == INV
+    assert step_gqa(lib, H=H, H_kv=H_kv, final=True, out=ptr(6)) == INV
+
+
+def test_gqa_valid_heads_reach_the_later_checks(lib):
+    # a valid grouping passes the head check and stops at the unsupported head size
+    for H, H_kv in ((4, 2), (8, 1), (5, 5)):
+        assert step_gqa(lib, H=H, H_kv=H_kv, d=96) == UNS
+        assert step_gqa(lib, H=H, H_kv=H_kv, d=96, final=True, out=ptr(6)) == UNS
+    assert step_gqa(lib, final=True, out=None) == INV
+    assert step_gqa(lib, final=True, out=ptr(0)) == INV  # out overlapping the queries
+
+
+def test_gqa_spans_use_the_kv_head_count(lib):
+    # one K/V head of 64 x 96 bf16 is 12 KiB: a state placed right after it does not
+    # overlap K with one K/V head, but would with four (d = 96 stops the call after the
+    # overlap checks)
+    a, b = _lib.segs([(0, 64)]), _lib.segs([(0, 64)])
+    k = ptr(1)
+    o_after_one_head = k + 64 * 96 * 2
+    args = lambda H_kv: (ptr(0), k, ptr(2), 1, 1, 4, H_kv, 64, 64, 96, ctypes.byref(a),
+                         ctypes.byref(b), 1, 0.1, 1, o_after_one_head, ptr(4), ptr(5), None)
+    assert lib.ra_step_gqa(*args(1)) == UNS
+    assert lib.ra_step_gqa(*args(4)) == INV

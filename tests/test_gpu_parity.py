@@ -413,3 +413,102 @@ def test_invalid_arguments_raise_before_launch(gpu_lib):
     with pytest.raises(_lib.RaError) as e:
         _lib.ra_step(q96, q96, q96, [(0, 64)], [(0, 64)], True, 0.1, st96.o, st96.m, st96.l)
     assert e.value.status == _lib.RA_ERR_UNSUPPORTED
+
+
+# ---- grouped K/V heads (fewer K/V heads than query heads) -------------------------
+
+GQA_CASES = [
+    # (B, H, H_kv, Lq, q_runs, Lk, k_runs, d, causal, dtype)
+    (2, 6, 2, 300, [(40, 137), (1000, 163)], 333, [(0, 250), (900, 83)], 128, True, torch.bfloat16),
+    (1, 4, 1, 517, [(0, 517)], 999, [(0, 999)], 64, False, torch.bfloat16),
+    (1, 8, 4, 640, [(0, 640)], 640, [(0, 640)], 128, True, torch.bfloat16),
+    (2, 4, 2, 190, [(64, 190)], 161, [(0, 161)], 64, True, torch.float32),
+    (1, 3, 1, 77, [(10, 40), (300, 37)], 250, [(0, 120), (200, 130)], 128, True, torch.float32),
+]
+
+
+def _gqa_inputs(ci, B, H, Hkv, Lq, Lk, d, dt):
+    q = seeded.gen_bhsd(200 + ci, 0, B, H, 0, Lq, d, dt, "cuda")
+    k = seeded.gen_bhsd(200 + ci, 1, B, Hkv, 0, Lk, d, dt, "cuda")
+    v = seeded.gen_bhsd(200 + ci, 2, B, Hkv, 0, Lk, d, dt, "cuda")
+    return q, k, v
+
+
+@pytest.mark.parametrize("ci", range(len(GQA_CASES)))
+def test_gqa_single_step(gpu_lib, ci):
+    B, H, Hkv, Lq, qr, Lk, kr, d, causal, dt = GQA_CASES[ci]
+    banner(f"gqa step case {ci}: B{B} H{H} H_kv{Hkv} Lq{Lq} Lk{Lk} d{d} causal={causal} {dt}")
+    q, k, v = _gqa_inputs(ci, B, H, Hkv, Lq, Lk, d, dt)
+    st = ring.RingState(B, H, Lq, d, "cuda")
+    scale = d ** -0.5
+    _lib.ra_step(q, k, v, qr, kr, causal, scale, st.o, st.m, st.l, init=True)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    _lib.ra_finalize(st.o, st.m, st.l, out, lse)
+    torch.cuda.synchronize()
+    qp, kp = _runs_pos(qr), _runs_pos(kr)
+    qc, kc, vc = (seeded.exact_f64(t.cpu()) for t in (q, k, v))
+    ro = np.zeros((B, H, Lq, d))
+    rl = np.zeros((B, H, Lq))
+    for b in range(B):
+        ro[b], rl[b] = oracle.grouped_attention(qc[b], qp, kc[b], vc[b], kp, scale, causal)
+    go, gl = out.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    empty = ~np.isfinite(rl)
+    assert np.array_equal(empty, ~np.isfinite(gl))
+    assert np.all(go[empty] == 0.0)
+    assert_close(go, ro, np.where(empty, 0.0, gl), np.where(empty, 0.0, rl), dt, f"gqa case {ci}")
+
+
+@pytest.mark.parametrize("ci", [0, 3])
+def test_gqa_step_final_equals_step_then_finalize(gpu_lib, ci):
+    B, H, Hkv, Lq, qr, Lk, kr, d, causal, dt = GQA_CASES[ci]
+    banner(f"gqa ra_step_final vs ra_step + ra_finalize, case {ci}")
+    q, k, v = _gqa_inputs(ci, B, H, Hkv, Lq, Lk, d, dt)
+    scale = d ** -0.5
+    a = ring.RingState(B, H, Lq, d, "cuda")
+    out1 = torch.empty_like(q)
+    lse1 = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    _lib.ra_step(q, k, v, qr, kr, causal, scale, a.o, a.m, a.l, init=True)
+    _lib.ra_finalize(a.o, a.m, a.l, out1, lse1)
+    b = ring.RingState(B, H, Lq, d, "cuda")
+    out2 = torch.empty_like(q)
+    lse2 = torch.empty_like(lse1)
+    _lib.ra_step_final(q, k, v, qr, kr, causal, scale, b.o, b.m, b.l, out2, lse2, init=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    fin = torch.isfinite(lse1)
+    assert torch.equal(fin, torch.isfinite(lse2))
+    assert (lse1[fin] - lse2[fin]).abs().max().item() <= 1e-5
+
+
+def test_gqa_with_one_kv_head_per_query_head_is_ra_step(gpu_lib):
+    banner("ra_step_gqa with H_kv = H vs ra_step: bitwise")
+    import ctypes
+    B, H, L, d = 1, 4, 300, 128
+    q, k, v = _gqa_inputs(9, B, H, H, L, L, d, torch.bfloat16)
+    a = ring.RingState(B, H, L, d, "cuda")
+    b = ring.RingState(B, H, L, d, "cuda")
+    _lib.ra_step(q, k, v, [(0, L)], [(0, L)], True, d ** -0.5, a.o, a.m, a.l, init=True)
+    qs, ks = _lib.segs([(0, L)]), _lib.segs([(0, L)])
+    st = _lib.load().ra_step_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), _lib.RA_BF16, B, H, H, L, L, d,
+                                 ctypes.byref(qs), ctypes.byref(ks), _lib.RA_MASK_CAUSAL, d ** -0.5,
+                                 _lib.RA_STEP_INIT, b.o.data_ptr(), b.m.data_ptr(), b.l.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == _lib.RA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(a.o, b.o) and torch.equal(a.m, b.m) and torch.equal(a.l, b.l)
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_gqa_causal_2rank_full(gpu_lib, rank):
+    w = configs.CAUSAL_2RANK_GQA
+    banner(f"{w.name} rank {rank} (H={w.H}, H_kv={w.Hkv})")
+    case = RingCase(w, rank)
+    assert case.kv[0][0].shape[1] == w.Hkv
+    out, lse = run_case(case)
+    ro, rl = case.expected()
+    assert_close(out.float().cpu().double().numpy(), ro, lse.cpu().double().numpy(), rl, w.dtype, w.name)
+
+
+def test_gqa_llm_32k_rank0_sampled(gpu_lib):
+    _sampled(configs.LLM_32K_CP4_GQA, 0)

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_rows, factored_spatial, factored_temporal, merge_lse
+from oracle import attention_rows, factored_spatial, factored_temporal, grouped_attention, merge_lse
 
 
 def brute_attention(q, q_pos, k, v, k_pos, scale, causal):
@@ -166,6 +166,53 @@ def test_matches_torch_sdpa_float64(causal):
     t = lambda a: torch.from_numpy(a)[None, None]
     ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal)
     np.testing.assert_allclose(o, ref[0, 0].numpy(), rtol=1e-11, atol=1e-12)
+
+
+# ---- grouped K/V heads ---------------------------------------------------------
+
+def test_grouped_constant_values_name_the_shared_head():
+    # closed form: if every value row of K/V head g equals g, each output row of
+    # query head h equals the index of the K/V head it reads, floor(h / G)
+    H, H_kv, n, S, d = 12, 3, 5, 9, 4
+    q, k = rnd(40, H, n, d, scale=2.0), rnd(41, H_kv, S, d, scale=2.0)
+    v = np.broadcast_to(np.arange(H_kv, dtype=np.float64)[:, None, None], (H_kv, S, 3)).copy()
+    pos = np.arange(S)
+    for causal in (False, True):
+        o, _ = grouped_attention(q, pos[-n:], k, v, pos, 0.7, causal)
+        for h in range(H):
+            np.testing.assert_allclose(o[h], np.full((n, 3), float(h * H_kv // H)), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(8, 2), (6, 3), (4, 1), (5, 5)])
+def test_grouped_matches_torch_sdpa_gqa_float64(causal, H, H_kv):
+    # library routine: PyTorch's scaled dot-product attention with enable_gqa,
+    # which shares each K/V head among consecutive query heads
+    L, d = 40, 8
+    q, k, v = rnd(42, H, L, d), rnd(43, H_kv, L, d), rnd(44, H_kv, L, d)
+    pos = np.arange(L)
+    o, _ = grouped_attention(q, pos, k, v, pos, 1.0 / math.sqrt(d), causal)
+    t = lambda a: torch.from_numpy(a)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal,
+                                                           enable_gqa=True)
+    np.testing.assert_allclose(o, ref[0].numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_grouped_with_one_group_per_head_is_per_head_attention():
+    H, n, S, d = 3, 6, 11, 5
+    q, k, v = rnd(45, H, n, d), rnd(46, H, S, d), rnd(47, H, S, d)
+    qp, kp = np.arange(5, 5 + n), np.arange(S)
+    o, lse = grouped_attention(q, qp, k, v, kp, 0.4, True)
+    for h in range(H):
+        bo, bl = brute_attention(q[h].tolist(), qp.tolist(), k[h].tolist(), v[h].tolist(),
+                                 kp.tolist(), 0.4, True)
+        np.testing.assert_allclose(o[h], bo, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[h], bl, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_rejects_heads_that_do_not_divide():
+    with pytest.raises(ValueError):
+        grouped_attention(rnd(48, 6, 2, 3), [0, 1], rnd(49, 4, 2, 3), rnd(50, 4, 2, 3), [0, 1], 1.0, False)
 
 
 def test_merge_identity_union_of_disjoint_key_sets():
