@@ -18,10 +18,12 @@ Sources (cited by page title and section):
   "Practical Use and Tradeoffs".
 * k8ai concepts, "Sequence and Context Parallel": "How context parallel works"
   (the ring figure and the causal balance remark), "Communication profile"
-  (ring volume and the number of K/V heads).
+  (ring volume and the number of K/V heads; exchanges in the forward and
+  the backward pass).
 """
 
 from .attention import (  # noqa: F401
+    attention_grads,
     attention_rows,
     factored_spatial,
     factored_temporal,

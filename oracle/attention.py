@@ -69,6 +69,49 @@ def attention_rows(q, q_pos, k, v, k_pos, scale, causal, row_chunk=256):
     return o, lse
 
 
+def attention_grads(q, q_pos, k, v, k_pos, scale, causal, do):
+    """Gradients of softmax attention with respect to its queries, keys and values.
+
+    The ring exchanges of the k8ai page ("Communication profile") happen in the
+    backward pass as well as the forward one, and the Ultralytics example
+    ("Practical Use and Tradeoffs") trains through the attention. The backward
+    pass computes the derivative of the same definition as ``attention_rows``;
+    for an upstream gradient do_i of each output row o_i (loss L with
+    dL/do_i = do_i):
+        P_ij  = exp(s_ij - lse_i) for visible j, 0 otherwise
+        dv_j  = sum_i P_ij do_i
+        dP_ij = <do_i, v_j>
+        ds_ij = P_ij (dP_ij - <do_i, o_i>)      (the softmax Jacobian)
+        dq_i  = scale * sum_j ds_ij k_j
+        dk_j  = scale * sum_i ds_ij q_i
+    Rows with no visible key contribute nothing.
+
+    q, do (n, d); k, v (S, d); other arguments as ``attention_rows``.
+    returns (dq (n, d), dk (S, d), dv (S, d)) in fp64
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    o, lse = attention_rows(q, q_pos, k, v, k_pos, scale, causal)
+    s = float(scale) * (q @ k.T)
+    visible = np.ones_like(s, dtype=bool)
+    if causal:
+        visible = k_pos[None, :] <= q_pos[:, None]
+    has_key = np.isfinite(lse)
+    lse_safe = np.where(has_key, lse, 0.0)
+    P = np.where(visible & has_key[:, None], np.exp(np.where(visible, s, 0.0) - lse_safe[:, None]), 0.0)
+    dv = P.T @ do
+    dP = do @ v.T
+    delta = np.sum(do * o, axis=1)
+    ds = P * (dP - delta[:, None])
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (ds.T @ q)
+    return dq, dk, dv
+
+
 def grouped_attention(q, q_pos, k, v, k_pos, scale, causal):
     """Attention of H query heads when groups of query heads share a K/V head.
 

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_rows, factored_spatial, factored_temporal, grouped_attention, merge_lse
+from oracle import (attention_grads, attention_rows, factored_spatial, factored_temporal,
+                    grouped_attention, merge_lse)
 
 
 def brute_attention(q, q_pos, k, v, k_pos, scale, causal):
@@ -166,6 +167,70 @@ def test_matches_torch_sdpa_float64(causal):
     t = lambda a: torch.from_numpy(a)[None, None]
     ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal)
     np.testing.assert_allclose(o, ref[0, 0].numpy(), rtol=1e-11, atol=1e-12)
+
+
+# ---- backward -----------------------------------------------------------------
+
+def _loss(q, qp, k, v, kp, scale, causal, do):
+    o, _ = attention_rows(q, qp, k, v, kp, scale, causal)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grads_match_central_differences(causal):
+    # the derivative of the forward definition, taken numerically: no formula shared
+    n, S, d = 4, 6, 3
+    q, k, v, do = rnd(60, n, d), rnd(61, S, d), rnd(62, S, d), rnd(63, n, d)
+    qp, kp = np.array([1, 3, 4, 5]), np.random.default_rng(64).permutation(S)
+    scale = 0.8
+    dq, dk, dv = attention_grads(q, qp, k, v, kp, scale, causal, do)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            lp = _loss(**{**args, name: xp}, qp=qp, kp=kp, scale=scale, causal=causal, do=do)
+            lm = _loss(**{**args, name: xm}, qp=qp, kp=kp, scale=scale, causal=causal, do=do)
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grads_match_torch_autograd_float64(causal):
+    # library routine: autograd through PyTorch's scaled dot-product attention
+    L, d = 48, 16
+    q, k, v, do = rnd(65, L, d), rnd(66, L, d), rnd(67, L, d), rnd(68, L, d)
+    pos = np.arange(L)
+    dq, dk, dv = attention_grads(q, pos, k, v, pos, 1.0 / math.sqrt(d), causal, do)
+    tq, tk, tv = (torch.from_numpy(a)[None, None].requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    out.backward(torch.from_numpy(do)[None, None])
+    for mine, ref in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, ref.grad[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_grads_invariants():
+    n, S, d = 7, 20, 4
+    q, k, v, do = rnd(69, n, d), rnd(70, S, d), rnd(71, S, d), rnd(72, n, d)
+    qp, kp = np.array([0, 4, 9, 11, 15, 18, 19]), np.arange(S)
+    dq, dk, dv = attention_grads(q, qp, k, v, kp, 0.6, True, do)
+    # linear in the upstream gradient
+    dq2, dk2, dv2 = attention_grads(q, qp, k, v, kp, 0.6, True, -2.5 * do)
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        np.testing.assert_allclose(b, -2.5 * a, rtol=1e-12, atol=1e-13)
+    # keys after the last query are never visible, so they receive no gradient
+    assert np.all(dk[kp > qp.max()] == 0) and np.all(dv[kp > qp.max()] == 0)
+    # adding one vector to every key shifts each row's scores by a constant, so
+    # the weights and dq do not change
+    u = rnd(73, d)
+    dq3, _, _ = attention_grads(q, qp, k + u, v, kp, 0.6, True, do)
+    np.testing.assert_allclose(dq3, dq, rtol=1e-9, atol=1e-11)
+    # unmasked: every row of ds sums to zero (softmax Jacobian), so sum_j dk_j = 0
+    _, dk4, _ = attention_grads(q, qp, k, v, kp, 0.6, False, do)
+    np.testing.assert_allclose(dk4.sum(axis=0), np.zeros(d), atol=1e-12)
 
 
 # ---- grouped K/V heads ---------------------------------------------------------
