@@ -19,9 +19,11 @@ RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
 RA_F32, RA_BF16 = 0, 1
 RA_MASK_NONE, RA_MASK_CAUSAL = 0, 1
 RA_STEP_INIT = 1
+RA_BWD_KV_INIT = 2
 
 # every symbol include/ra.h declares
 EXPORTS = ("ra_step", "ra_finalize", "ra_step_final", "ra_step_gqa", "ra_step_final_gqa",
+           "ra_bwd_prep", "ra_step_bwd",
            "ra_merge_lse", "ra_factored_spatial",
            "ra_factored_temporal", "ra_kv_pass", "ra_status_string",
            "ra_last_hip_error", "ra_version")
@@ -52,6 +54,10 @@ _SIGS = {
     "ra_step_final_gqa": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                  ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
                                  _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ra_bwd_prep": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "ra_step_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                           ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
+                           _vp, _vp, _vp, _vp]),
     "ra_finalize": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "ra_step_final": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                              ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
@@ -157,6 +163,24 @@ def ra_step_final(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, out, lse
     else:
         _check("ra_step_final_gqa", load().ra_step_final_gqa(_p(q), _p(k), _p(v), _dtype(q), B, H,
                                                              H_kv, Lq, Lk, d, *args))
+
+
+def ra_bwd_prep(out, dout, delta, stream=None):
+    B, H, L, d = out.shape
+    _check("ra_bwd_prep", load().ra_bwd_prep(_p(out), _p(dout), _dtype(out), B, H, L, d, _p(delta),
+                                             _s(stream)))
+
+
+def ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs, causal, scale, dq, dk, dv,
+                init_dq=False, init_dkv=False, stream=None):
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    qs, ks = segs(q_segs), segs(kv_segs)
+    flags = (RA_STEP_INIT if init_dq else 0) | (RA_BWD_KV_INIT if init_dkv else 0)
+    _check("ra_step_bwd", load().ra_step_bwd(
+        _p(q), _p(k), _p(v), _p(dout), _p(lse), _p(delta), _dtype(q), B, H, Lq, Lk, d,
+        ctypes.byref(qs), ctypes.byref(ks), RA_MASK_CAUSAL if causal else RA_MASK_NONE,
+        float(scale), flags, _p(dq), _p(dk), _p(dv), _s(stream)))
 
 
 def ra_finalize(o_acc, m, l, out, lse=None, stream=None):

@@ -1,0 +1,542 @@
+// Backward ring step on the gfx950 matrix cores (bf16 in, fp32 accumulate).
+//
+// The ring moves K/V blocks in the backward pass as in the forward one (k8ai
+// "Sequence and Context Parallel", "Communication profile"); the Ultralytics
+// glossary's example trains through the attention ("Practical Use and
+// Tradeoffs"). For one block held at a ring step, this adds the block's share
+// of the gradients of softmax attention, taken with the final forward
+// normaliser lse_i and delta_i = <dO_i, O_i>:
+//   P_ij  = exp(scale <q_i, k_j> - lse_i)   (visible pairs only)
+//   dS_ij = P_ij (<dO_i, v_j> - delta_i)
+//   dQ_i += scale sum_j dS_ij k_j      (local queries: dQ stays on the device)
+//   dK_j += scale sum_i dS_ij q_i      (the block's accumulators travel with it)
+//   dV_j += sum_i P_ij dO_i
+//
+// Two kernels, no atomics, so the result is deterministic:
+// * bwd_dq: each wave owns 32 query rows and streams 64-key K/V tiles:
+//   S^T = K Q^T and dP^T = V dO^T (A from LDS, B = the wave's Q and dO rows
+//   in registers), dS^T formed in registers (every lane owns one query, so
+//   lse and delta are lane scalars), dQ^T += K^T dS^T with the transposing
+//   LDS read for K^T and dS^T as the B operand straight from the registers.
+// * bwd_dkdv: each wave owns 32 key rows and streams 64-row Q/dO tiles:
+//   S = Q K^T and dP = dO V^T (every lane owns one key; the per-row lse and
+//   delta of the tile come from LDS), then dV^T += dO^T P and dK^T += Q^T dS.
+// Both recompute S and dP, so the matrix cores run 14*d FLOP per visible
+// pair against the 8*d of the four products the gradients need.
+// The LDS tile layout, the operand reads and the key permutation inside each
+// 16-row MFMA slice are those of the forward ring step: tiles are stored
+// column-major in 16-byte columns (runs of 64 rows padded to 1088 bytes),
+// filled by bounds-checked buffer loads that write LDS directly.
+
+#include "ra_bwd.h"
+#include "ra_device.h"
+
+namespace ra {
+namespace {
+
+constexpr int kBW = 4;                // waves per workgroup
+constexpr int kBThreads = 64 * kBW;
+constexpr int kOwn = 32 * kBW;        // owned rows per workgroup
+constexpr int kT = 64;                // streamed rows per tile
+constexpr int kRunB = 1088;           // LDS bytes per 64-row run of one 16-byte column
+constexpr int kXcdsB = 8;
+
+template <int D>
+struct BLay {
+  static constexpr int NRUN = D / 8;               // 16-byte columns = load runs per tile
+  static constexpr int TBYTES = NRUN * kRunB;      // one tensor's tile
+  static constexpr int RUNS_PER_WAVE = NRUN / kBW;
+  static constexpr int ROWV = 2 * kT * 4;          // lse (log2 units) and delta of a tile's rows
+  static constexpr int STAGE = 2 * TBYTES + ROWV;
+  static_assert(NRUN % kBW == 0, "runs must split evenly over the waves");
+  static constexpr int at(int row, int col) { return col * kRunB + 16 * row; }
+};
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_b;
+typedef __attribute__((address_space(3))) char lds_char_b;
+
+// 16 bytes per lane from a bounds-checked buffer straight into LDS at
+// m0 + 16*lane; out-of-range rows read as zero. Ordered by explicit vmcnt
+// waits before the barriers that publish a tile.
+__device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t rs, const char* lds, int voff,
+                                            int soff) {
+  const unsigned m0 = (unsigned)(size_t)(const lds_char_b*)lds;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
+               : "memory");
+}
+
+__device__ __forceinline__ bf16x8 bl_b128(const char* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ bf16x4 bl_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b*)p);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const bf16* base, int32_t rows, int d) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, rows * d * 2, 0x00020000);
+}
+
+// rows row0.. of a [rows, D] slice into a tile of the layout above; wave w
+// fills runs (16-byte columns) w*RUNS_PER_WAVE.., lane i brings row i
+template <int D>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* dst, int32_t row0, int w,
+                                          int lane) {
+  using L = BLay<D>;
+#pragma unroll
+  for (int i = 0; i < L::RUNS_PER_WAVE; ++i) {
+    const int r = w * L::RUNS_PER_WAVE + i;
+    bload_lds16(rs, dst + r * kRunB, lane * D * 2 + 16 * r, row0 * D * 2);
+  }
+}
+
+// A operand of rows 32st+l32 of a tile, d columns 16ksi+8h..+8
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const char* tile, int st, int ksi, int l32, int h) {
+  return bl_b128(tile + BLay<D>::at(32 * st + l32, 2 * ksi + h));
+}
+
+// A operand of the transposed tile: d rows 32t.. and the 16 tile rows of
+// slice kc, in the permuted order that matches a score accumulator packed by
+// pack_b (lane base `tr` from tr_base)
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, int tr, int kc, int t) {
+  const int off = tr + BLay<D>::at(16 * kc, 4 * t);
+  const bf16x4 a = bl_tr16(tile + off);
+  const bf16x4 b = bl_tr16(tile + off + 16 * 8);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <int D>
+__device__ __forceinline__ int tr_base(int lane) {
+  const int g = lane >> 4, jj = lane & 15, rr = jj >> 2, c4 = jj & 3;
+  return BLay<D>::at(4 * (g >> 1) + rr, 2 * (g & 1) + (c4 >> 1)) + 8 * (c4 & 1);
+}
+
+// the 16 values of one 32x32 accumulator as two bf16 B operands (16-row slices)
+__device__ __forceinline__ void pack_b(const f32x16& x, bf16x8& lo, bf16x8& hi) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    lo[r] = to_bf16(x[r]);
+    hi[r] = to_bf16(x[8 + r]);
+  }
+}
+
+// row of register r of a 32x32 accumulator (within its 32-row block), for lane half h
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r / 4) + 4 * h + (r % 4); }
+
+// logical workgroup index: each XCD takes a contiguous range, so the
+// workgroups of one slice share that XCD's L2
+__device__ __forceinline__ int32_t xcd_logical(int32_t per_xcd) {
+  return (int32_t)(blockIdx.x % kXcdsB) * per_xcd + (int32_t)(blockIdx.x / kXcdsB);
+}
+
+// Tiles [first, last) of `rows` streamed rows (segments `ss`) holding rows
+// whose position is >= lo (causal: rows that some owned row can see, or that
+// can see some owned row), as at most two runs of tile indices.
+struct TileRuns {
+  int32_t t0a, n0, t1a, n;
+};
+__device__ __forceinline__ TileRuns tiles_from(const DevSegs& ss, int32_t rows, int32_t lo_pos,
+                                               int32_t hi_pos, bool after) {
+  // after: keep rows with pos >= lo_pos (queries seen by keys);
+  // otherwise keep rows with pos <= hi_pos (keys seen by queries)
+  int32_t ra0, rb0, ra1 = 0, rb1 = 0;
+  const int32_t len1 = rows - ss.len0;
+  auto clampi = [](int32_t x, int32_t n) { return x < 0 ? 0 : (x > n ? n : x); };
+  if (after) {
+    ra0 = clampi(lo_pos - ss.start0, ss.len0);
+    rb0 = ss.len0;
+    if (len1 > 0) {
+      ra1 = ss.len0 + clampi(lo_pos - ss.start1, len1);
+      rb1 = rows;
+    }
+  } else {
+    ra0 = 0;
+    rb0 = clampi(hi_pos - ss.start0 + 1, ss.len0);
+    if (len1 > 0) {
+      ra1 = ss.len0;
+      rb1 = ss.len0 + clampi(hi_pos - ss.start1 + 1, len1);
+    }
+  }
+  TileRuns tr;
+  const int32_t t0b = (rb0 + kT - 1) / kT;
+  tr.t0a = ra0 / kT;
+  tr.n0 = rb0 > ra0 ? t0b - tr.t0a : 0;
+  tr.t1a = ra1 / kT;
+  const int32_t t1b = (rb1 + kT - 1) / kT;
+  if (tr.n0 > 0 && tr.t1a < t0b) tr.t1a = t0b;
+  const int32_t n1 = rb1 > ra1 && t1b > tr.t1a ? t1b - tr.t1a : 0;
+  tr.n = tr.n0 + n1;
+  return tr;
+}
+__device__ __forceinline__ int32_t tile_row0(const TileRuns& tr, int32_t n) {
+  return (n < tr.n0 ? tr.t0a + n : tr.t1a + (n - tr.n0)) * kT;
+}
+
+// s_waitcnt vmcnt(0) (gfx9 encoding, other counters left alone)
+constexpr int kVmcnt0 = (7 << 4) | (15 << 8);
+
+// ---------------------------------------------------------------------------
+// dQ: owned queries, streamed K/V tiles
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
+    int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, float scale,
+    int32_t init, float* __restrict__ dQ, int32_t nqt, int32_t per_xcd) {
+  using L = BLay<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int32_t logical = xcd_logical(per_xcd);
+  if (logical >= nb * nqt) return;
+  const int32_t prob = logical / nqt;
+  const int32_t q0 = (logical - prob * nqt) * kOwn;
+
+  const int32_t w_r0 = q0 + 32 * w;
+  const int32_t qrow = w_r0 + l32;
+  const bool qvalid = qrow < Lq;
+  const int32_t qrow_c = qvalid ? qrow : Lq - 1;
+  const int32_t qpos = seg_pos(qs, qrow_c);
+  int32_t w_qlo = INT32_MAX, w_qhi;
+  if (w_r0 < Lq) seg_range(qs, w_r0, min(w_r0 + 32, Lq), w_qlo, w_qhi);
+  w_qlo = __builtin_amdgcn_readfirstlane(w_qlo);
+
+  // key tiles some owned query can see
+  TileRuns tr{0, 0, 0, 0};
+  if (CAUSAL) {
+    int32_t lo, hi;
+    seg_range(qs, q0, min(q0 + kOwn, Lq), lo, hi);
+    tr = tiles_from(ks, Lk, 0, hi, false);
+  } else {
+    tr.n0 = tr.n = (Lk + kT - 1) / kT;
+  }
+  const size_t rbase = (size_t)prob * Lq;
+  float* dqp = dQ + (rbase + qrow) * D + 4 * h;
+  if (tr.n == 0) {
+    if (init && qvalid) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(f32x4*)(dqp + 32 * t + 8 * i) = f32x4{};
+    }
+    return;
+  }
+
+  const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + (size_t)prob * Lk * D, Lk, D);
+  const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + (size_t)prob * Lk * D, Lk, D);
+  auto fetch = [&](int32_t n) {
+    char* st = smem + (n & 1) * L::STAGE;
+    const int32_t r0 = tile_row0(tr, n);
+    load_tile<D>(krs, st, r0, w, lane);
+    load_tile<D>(vrs, st + L::TBYTES, r0, w, lane);
+  };
+  fetch(0);
+
+  // this lane's query and upstream-gradient rows (B operands), lse and delta
+  bf16x8 qf[KS], df[KS];
+  const bf16* qp = Q + (rbase + qrow_c) * D + 8 * h;
+  const bf16* dp = dO + (rbase + qrow_c) * D + 8 * h;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = *(const bf16x8*)(qp + 16 * s);
+    df[s] = *(const bf16x8*)(dp + 16 * s);
+  }
+  const float lse = Lse[rbase + qrow_c];
+  // rows with no visible key (lse = -inf) and rows past the end get P = 0
+  const float lse2 = (qvalid && lse != kNegInf) ? lse * kLog2e : __builtin_inff();
+  const float dlt = Dlt[rbase + qrow_c];
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
+  const int trb = tr_base<D>(lane);
+
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  for (int32_t n = 0; n < tr.n; ++n) {
+    if (n + 1 < tr.n) fetch(n + 1);
+    const char* kt = smem + (n & 1) * L::STAGE;
+    const char* vt = kt + L::TBYTES;
+    const int32_t kt0 = tile_row0(tr, n);
+    // element mask: the ragged tail of the block, and (causal) keys after
+    // some query of this wave
+    bool need_mask = kt0 + kT > Lk;
+    if (CAUSAL) {
+      int32_t klo, khi;
+      seg_range(ks, kt0, min(kt0 + kT, Lk), klo, khi);
+      (void)klo;
+      need_mask = need_mask || khi > w_qlo;
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      f32x16 s = f32x16{}, dpv = f32x16{};
+#pragma unroll
+      for (int ksi = 0; ksi < KS; ++ksi) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(kt, st, ksi, l32, h), qf[ksi], s, 0, 0, 0);
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vt, st, ksi, l32, h), df[ksi], dpv, 0, 0, 0);
+      }
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[r], c_log2, -lse2));
+        if (need_mask) {
+          const int32_t kr = kt0 + 32 * st + acc_row(r, h);
+          const bool vis = kr < Lk && (!CAUSAL || seg_pos(ks, kr) <= qpos);
+          p = vis ? p : 0.f;
+        }
+        ds[r] = p * (dpv[r] - dlt);
+      }
+      bf16x8 b0, b1;
+      pack_b(ds, b0, b1);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, trb, 2 * st, t), b0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, trb, 2 * st + 1, t), b1, acc[t], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+  }
+  if (!qvalid) return;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 y = {scale * acc[t][4 * i], scale * acc[t][4 * i + 1], scale * acc[t][4 * i + 2],
+                 scale * acc[t][4 * i + 3]};
+      if (!init) y += *(const f32x4*)(dqp + 32 * t + 8 * i);
+      *(f32x4*)(dqp + 32 * t + 8 * i) = y;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: owned keys, streamed Q/dO tiles
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
+    int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, float scale,
+    int32_t init, float* __restrict__ dK, float* __restrict__ dV, int32_t nkt, int32_t per_xcd) {
+  using L = BLay<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int32_t logical = xcd_logical(per_xcd);
+  if (logical >= nb * nkt) return;
+  const int32_t prob = logical / nkt;
+  const int32_t k0 = (logical - prob * nkt) * kOwn;
+
+  const int32_t w_r0 = k0 + 32 * w;
+  const int32_t krow = w_r0 + l32;
+  const bool kvalid = krow < Lk;
+  const int32_t krow_c = kvalid ? krow : Lk - 1;
+  const int32_t kpos = seg_pos(ks, krow_c);
+  int32_t w_klo, w_khi = INT32_MIN;
+  if (w_r0 < Lk) seg_range(ks, w_r0, min(w_r0 + 32, Lk), w_klo, w_khi);
+  w_khi = __builtin_amdgcn_readfirstlane(w_khi);
+
+  // query tiles holding a query that can see some owned key
+  TileRuns tr{0, 0, 0, 0};
+  if (CAUSAL) {
+    int32_t lo, hi;
+    seg_range(ks, k0, min(k0 + kOwn, Lk), lo, hi);
+    tr = tiles_from(qs, Lq, lo, 0, true);
+  } else {
+    tr.n0 = tr.n = (Lq + kT - 1) / kT;
+  }
+  const size_t kb = (size_t)prob * Lk;
+  float* dkp = dK + (kb + krow) * D + 4 * h;
+  float* dvp = dV + (kb + krow) * D + 4 * h;
+  if (tr.n == 0) {
+    if (init && kvalid) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *(f32x4*)(dkp + 32 * t + 8 * i) = f32x4{};
+          *(f32x4*)(dvp + 32 * t + 8 * i) = f32x4{};
+        }
+    }
+    return;
+  }
+
+  const size_t rbase = (size_t)prob * Lq;
+  const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(Q + rbase * D, Lq, D);
+  const __amdgpu_buffer_rsrc_t drs = slice_rsrc(dO + rbase * D, Lq, D);
+  // lse (log2 units) and delta of the tile's rows: thread i < 64 brings the
+  // lse of row i, thread 64 + i its delta; rows past the end get lse = +inf
+  // (so P = 0) and delta = 0
+  float rowv = 0.f;
+  auto fetch_rowv = [&](int32_t n) {
+    const int32_t r = tile_row0(tr, n) + (tid & 63);
+    if (tid < 64) {
+      const float x = r < Lq ? Lse[rbase + r] : kNegInf;
+      rowv = x != kNegInf ? x * kLog2e : __builtin_inff();
+    } else if (tid < 128) {
+      rowv = r < Lq ? Dlt[rbase + r] : 0.f;
+    }
+  };
+  auto store_rowv = [&](int32_t n) {
+    if (tid < 128) *(float*)(smem + (n & 1) * L::STAGE + 2 * L::TBYTES + 4 * tid) = rowv;
+  };
+  auto fetch = [&](int32_t n) {
+    char* st = smem + (n & 1) * L::STAGE;
+    const int32_t r0 = tile_row0(tr, n);
+    load_tile<D>(qrs, st, r0, w, lane);
+    load_tile<D>(drs, st + L::TBYTES, r0, w, lane);
+  };
+  fetch_rowv(0);
+  fetch(0);
+
+  bf16x8 kf[KS], vf[KS];
+  const bf16* kp = K + (kb + krow_c) * D + 8 * h;
+  const bf16* vp = V + (kb + krow_c) * D + 8 * h;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = *(const bf16x8*)(kp + 16 * s);
+    vf[s] = *(const bf16x8*)(vp + 16 * s);
+  }
+  f32x16 ak[DT], av[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) ak[t] = av[t] = f32x16{};
+  const int trb = tr_base<D>(lane);
+
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  store_rowv(0);
+  __syncthreads();
+  for (int32_t n = 0; n < tr.n; ++n) {
+    if (n + 1 < tr.n) {
+      fetch_rowv(n + 1);
+      fetch(n + 1);
+    }
+    const char* qt = smem + (n & 1) * L::STAGE;
+    const char* dt = qt + L::TBYTES;
+    const float* lsev = (const float*)(qt + 2 * L::TBYTES);
+    const float* dltv = lsev + kT;
+    const int32_t qt0 = tile_row0(tr, n);
+    bool need_mask = false;
+    if (CAUSAL) {
+      int32_t qlo, qhi;
+      seg_range(qs, qt0, min(qt0 + kT, Lq), qlo, qhi);
+      (void)qhi;
+      need_mask = w_khi > qlo;
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      f32x16 s = f32x16{}, dpv = f32x16{};
+#pragma unroll
+      for (int ksi = 0; ksi < KS; ++ksi) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qt, st, ksi, l32, h), kf[ksi], s, 0, 0, 0);
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(dt, st, ksi, l32, h), vf[ksi], dpv, 0, 0, 0);
+      }
+      f32x16 p, ds;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rb = 32 * st + 8 * i + 4 * h;  // rows rb..rb+3 of the tile
+        const f32x4 l4 = *(const f32x4*)(lsev + rb);
+        const f32x4 d4 = *(const f32x4*)(dltv + rb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * i + j;
+          float pv = fast_exp2(__builtin_fmaf(s[r], c_log2, -l4[j]));
+          if (need_mask) {
+            const int32_t q = qt0 + rb + j;
+            const bool vis = q < Lq && seg_pos(qs, q) >= kpos;
+            pv = vis ? pv : 0.f;
+          }
+          p[r] = pv;
+          ds[r] = pv * (dpv[r] - d4[j]);
+        }
+      }
+      bf16x8 p0, p1, s0, s1;
+      pack_b(p, p0, p1);
+      pack_b(ds, s0, s1);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        av[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dt, trb, 2 * st, t), p0, av[t], 0, 0, 0);
+        av[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dt, trb, 2 * st + 1, t), p1, av[t], 0, 0, 0);
+        ak[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qt, trb, 2 * st, t), s0, ak[t], 0, 0, 0);
+        ak[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qt, trb, 2 * st + 1, t), s1, ak[t], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    if (n + 1 < tr.n) store_rowv(n + 1);
+    __syncthreads();
+  }
+  if (!kvalid) return;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 yk = {scale * ak[t][4 * i], scale * ak[t][4 * i + 1], scale * ak[t][4 * i + 2],
+                  scale * ak[t][4 * i + 3]};
+      f32x4 yv = {av[t][4 * i], av[t][4 * i + 1], av[t][4 * i + 2], av[t][4 * i + 3]};
+      if (!init) {
+        yk += *(const f32x4*)(dkp + 32 * t + 8 * i);
+        yv += *(const f32x4*)(dvp + 32 * t + 8 * i);
+      }
+      *(f32x4*)(dkp + 32 * t + 8 * i) = yk;
+      *(f32x4*)(dvp + 32 * t + 8 * i) = yv;
+    }
+}
+
+// delta_i = <dO_i, O_i> in fp32; D/8 lanes per row, 8 elements each
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ O,
+                                                       const bf16* __restrict__ dO, int64_t rows,
+                                                       float* __restrict__ Dlt) {
+  constexpr int LPR = D / 8;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = g / LPR;
+  const int part = (int)(g % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 a = *(const bf16x8*)(O + row * D + 8 * part);
+    const bf16x8 b = *(const bf16x8*)(dO + row * D + 8 * part);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_fmaf(from_bf16(a[j]), from_bf16(b[j]), acc);
+  }
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && part == 0) Dlt[row] = acc;
+}
+
+DevSegs bdev(const HostSegs& s) { return DevSegs{s.start0, s.start1, s.len0, s.len}; }
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+  const float c = a.scale * kLog2e;
+  const int32_t nqt = (a.Lq + kOwn - 1) / kOwn, nkt = (a.Lk + kOwn - 1) / kOwn;
+  const int32_t pq = (int32_t)(((int64_t)a.nb * nqt + kXcdsB - 1) / kXcdsB);
+  const int32_t pk = (int32_t)(((int64_t)a.nb * nkt + kXcdsB - 1) / kXcdsB);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(kXcdsB * pq), dim3(kBThreads), 0, st,
+                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
+                     a.lse, a.delta, a.nb, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
+                     (int32_t)a.init_dq, a.dq, nqt, pq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(kXcdsB * pk), dim3(kBThreads), 0, st,
+                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
+                     a.lse, a.delta, a.nb, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
+                     (int32_t)a.init_dkv, a.dk, a.dv, nkt, pk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_step_bwd_bf16(const BwdArgs& a, hipStream_t st) {
+  if (a.d == 128) return a.causal ? launch_bwd<128, true>(a, st) : launch_bwd<128, false>(a, st);
+  return a.causal ? launch_bwd<64, true>(a, st) : launch_bwd<64, false>(a, st);
+}
+
+hipError_t launch_bwd_prep_bf16(const void* out, const void* dout, int64_t rows, int32_t d,
+                                float* delta, hipStream_t st) {
+  const int64_t threads = rows * (d / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, st, (const bf16*)out, (const bf16*)dout, rows, delta);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, st, (const bf16*)out, (const bf16*)dout, rows, delta);
+  return hipGetLastError();
+}
+
+}  // namespace ra

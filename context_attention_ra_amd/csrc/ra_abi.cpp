@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "ra_bwd.h"
 #include "ra_launch.h"
 
 namespace {
@@ -163,6 +164,68 @@ ra_status ra_step_final(const void* q, const void* k, const void* v, ra_dtype dt
                         hipStream_t stream) {
   return ra_step_final_gqa(q, k, v, dt, B, H, H, Lq, Lk, d, q_segs, kv_segs, mask, scale, flags,
                            o_acc, m, l, out, lse, stream);
+}
+
+ra_status ra_bwd_prep(const void* out, const void* dout, ra_dtype dt, int32_t B, int32_t H,
+                      int32_t L, int32_t d, float* delta, hipStream_t stream) {
+  if (!out || !dout || !delta) return RA_ERR_INVALID_ARG;
+  if (!known_dtype(dt) || !dims_ok(B, H, L) || d <= 0) return RA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(delta, 4)) return RA_ERR_INVALID_ARG;
+  const size_t rows = (size_t)B * H * L;
+  const Range rd = span(delta, rows * 4);
+  if (overlap(rd, span(out, rows * d * esize(dt))) || overlap(rd, span(dout, rows * d * esize(dt))))
+    return RA_ERR_INVALID_ARG;
+  if (dt != RA_BF16 || !supported_d(d)) return RA_ERR_UNSUPPORTED;
+  return hip_fail(ra::launch_bwd_prep_bf16(out, dout, (int64_t)rows, d, delta, stream));
+}
+
+ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, const float* delta, ra_dtype dt, int32_t B, int32_t H,
+                      int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
+                      const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
+                      float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream) {
+  if (!dout || !lse || !delta || !dq_acc || !dk_acc || !dv_acc) return RA_ERR_INVALID_ARG;
+  if (flags & ~(RA_STEP_INIT | RA_BWD_KV_INIT)) return RA_ERR_INVALID_ARG;
+  // the forward checks cover q, k, v, the sizes, segments, mask and scale; dq_acc
+  // and the two per-row vectors take the places of o_acc, m and l
+  ra::StepArgs sa;
+  const ra_status st = step_args(q, k, v, dt, B, H, H, Lq, Lk, d, q_segs, kv_segs, mask, scale,
+                                 flags & RA_STEP_INIT, dq_acc, (float*)lse, (float*)delta, &sa);
+  if (st != RA_OK) return st;
+  if (!aligned(dout, 16) || !aligned(dk_acc, 16) || !aligned(dv_acc, 16)) return RA_ERR_INVALID_ARG;
+  const size_t nb = (size_t)B * H, es = esize(dt);
+  const Range in[] = {span(q, nb * Lq * d * es), span(k, nb * Lk * d * es), span(v, nb * Lk * d * es),
+                      span(dout, nb * Lq * d * es), span(lse, nb * Lq * 4), span(delta, nb * Lq * 4)};
+  const Range acc[] = {span(dq_acc, nb * Lq * d * 4), span(dk_acc, nb * Lk * d * 4),
+                       span(dv_acc, nb * Lk * d * 4)};
+  for (int i = 0; i < 3; ++i) {
+    for (Range x : in)
+      if (overlap(acc[i], x)) return RA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(acc[i], acc[j])) return RA_ERR_INVALID_ARG;
+  }
+  if (dt != RA_BF16) return RA_ERR_UNSUPPORTED;
+  ra::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.nb = sa.nb;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.d = d;
+  a.qs = sa.qs;
+  a.ks = sa.ks;
+  a.causal = sa.causal;
+  a.init_dq = (flags & RA_STEP_INIT) != 0;
+  a.init_dkv = (flags & RA_BWD_KV_INIT) != 0;
+  a.scale = scale;
+  a.dq = dq_acc;
+  a.dk = dk_acc;
+  a.dv = dv_acc;
+  return hip_fail(ra::launch_step_bwd_bf16(a, stream));
 }
 
 ra_status ra_finalize(const float* o_acc, const float* m, const float* l, int32_t B, int32_t H,

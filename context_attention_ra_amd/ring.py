@@ -134,3 +134,55 @@ def run(q: torch.Tensor,
             ev_free[s % 2].record(compute)
             used[s % 2] = True
     return out, lse, state
+
+
+def run_bwd(q: torch.Tensor,
+            q_segs: Sequence[Tuple[int, int]],
+            kv_blocks: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+            kv_segs: Sequence[Sequence[Tuple[int, int]]],
+            rank: int,
+            causal: bool,
+            out: torch.Tensor,
+            lse: torch.Tensor,
+            dout: torch.Tensor,
+            scale: Optional[float] = None,
+            order: Optional[List[int]] = None,
+            dkv: Optional[List[Tuple[torch.Tensor, torch.Tensor]]] = None):
+    """Backward pass of rank `rank`'s share: P backward block steps.
+
+    The ring passes the K/V blocks again in the backward pass (k8ai
+    "Communication profile"), each now travelling with its dK/dV
+    accumulators. At step s the rank adds its queries' contributions to the
+    block of rank order[s] with ``ra_step_bwd``; dQ stays local.
+
+    out, lse   the final forward output and lse of the local queries
+    dout       upstream gradient of `out`
+    dkv        optional per-block (dk, dv) fp32 accumulators [B, H, Lk, d] that
+               already hold other ranks' contributions (they are added to);
+               None: fresh accumulators holding this rank's contributions only
+    returns (dq [B, H, Lq, d] fp32, dkv)
+    """
+    P = len(kv_blocks)
+    if order is None:
+        order = layout.ring_order(rank, P)
+    if sorted(order) != list(range(P)):
+        raise ValueError("order must visit every block once")
+    B, H, Lq, d = q.shape
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    stream = torch.cuda.current_stream(dev)
+    fresh = dkv is None
+    if fresh:
+        dkv = [(torch.empty(k.shape, dtype=torch.float32, device=dev),
+                torch.empty(k.shape, dtype=torch.float32, device=dev)) for k, _ in kv_blocks]
+    delta = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+    _lib.ra_bwd_prep(out, dout, delta, stream=stream)
+    dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device=dev)
+    for s in range(P):
+        t = order[s]
+        k, v = kv_blocks[t]
+        dk, dv = dkv[t]
+        _lib.ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs[t], causal, scale, dq, dk, dv,
+                         init_dq=(s == 0), init_dkv=fresh, stream=stream)
+    return dq, dkv

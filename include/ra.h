@@ -174,6 +174,56 @@ ra_status ra_step_final_gqa(const void* q, const void* k, const void* v, ra_dtyp
                             ra_mask mask, float scale, uint32_t flags, float* o_acc,
                             float* m, float* l, void* out, float* lse, hipStream_t stream);
 
+/* ra_step_bwd flag: the block's gradient accumulators dk_acc, dv_acc start at
+ * zero; they are not read, only written. (RA_STEP_INIT does the same for
+ * dq_acc.) */
+#define RA_BWD_KV_INIT 2u
+
+/*
+ * ra_bwd_prep — per-row delta_i = <dO_i, O_i> (fp32) of the final forward
+ * output O and its upstream gradient dO, needed by every backward ring step.
+ * out, dout [B,H,L,d] of dt (RA_BF16); delta [B,H,L] fp32.
+ * Errors: RA_ERR_INVALID_ARG for null pointers, sizes <= 0 or delta
+ *   overlapping the inputs; RA_ERR_UNSUPPORTED for dt != RA_BF16 or d not in
+ *   {64, 128}.
+ */
+ra_status ra_bwd_prep(const void* out, const void* dout, ra_dtype dt, int32_t B, int32_t H,
+                      int32_t L, int32_t d, float* delta, hipStream_t stream);
+
+/*
+ * ra_step_bwd — one backward ring step. The ring passes K/V blocks in the
+ * backward pass as well (k8ai "Communication profile"); at each step the
+ * device adds the gradient contributions of its local queries against the
+ * block it holds: with P_ij = exp(scale <q_i, k_j> - lse_i) over the visible
+ * pairs and dS_ij = P_ij (<dO_i, v_j> - delta_i),
+ *   dq_acc_i += scale sum_j dS_ij k_j   (stays with the local queries)
+ *   dk_acc_j += scale sum_i dS_ij q_i   (travels with the block)
+ *   dv_acc_j += sum_i P_ij dO_i         (travels with the block)
+ * Summed over the P blocks (dq) and over the P ranks' queries (dk, dv) these
+ * are the exact gradients of the attention, whatever the order.
+ * q, dout  [B,H,Lq,d] local queries and the upstream gradient of their output
+ * k, v     [B,H,Lk,d] the block held at this step
+ * lse      [B,H,Lq] fp32, the final forward lse of the local queries
+ *          (ra_step_final / ra_finalize); -inf rows contribute nothing
+ * delta    [B,H,Lq] fp32 from ra_bwd_prep
+ * q_segs, kv_segs, mask, scale: as for ra_step (the same mask and scale as
+ *          the forward pass)
+ * flags    0, RA_STEP_INIT (dq_acc starts at zero), RA_BWD_KV_INIT (dk_acc,
+ *          dv_acc start at zero), or both
+ * dq_acc   [B,H,Lq,d] fp32 in/out; dk_acc, dv_acc [B,H,Lk,d] fp32 in/out
+ * dt must be RA_BF16 (inputs bf16, products on the matrix cores, fp32
+ * accumulation). The two kernels run one after the other on `stream`.
+ * Errors: those of ra_step, RA_ERR_INVALID_ARG for a null dout, lse, delta or
+ *   accumulator, unknown flags, or an accumulator overlapping an input or
+ *   another accumulator; RA_ERR_UNSUPPORTED for dt != RA_BF16.
+ */
+ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, const float* delta, ra_dtype dt,
+                      int32_t B, int32_t H, int32_t Lq, int32_t Lk, int32_t d,
+                      const ra_segs* q_segs, const ra_segs* kv_segs, ra_mask mask,
+                      float scale, uint32_t flags, float* dq_acc, float* dk_acc,
+                      float* dv_acc, hipStream_t stream);
+
 /*
  * ra_merge_lse — combine two normalised partial attentions of the same queries
  * over disjoint key sets (the partial outputs the Day 83 post's devices

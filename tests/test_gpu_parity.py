@@ -512,3 +512,161 @@ def test_gqa_causal_2rank_full(gpu_lib, rank):
 
 def test_gqa_llm_32k_rank0_sampled(gpu_lib):
     _sampled(configs.LLM_32K_CP4_GQA, 0)
+
+
+# ---- backward ring step -------------------------------------------------------------
+
+DOUT = 3  # seeded tensor id of the upstream gradient
+
+
+def grad_close(gpu, ref, what):
+    """Gradients are not bounded like outputs: errors are taken relative to the
+    gradient's own scale (max |ref|) and in aggregate (sum |diff| / sum |ref|)."""
+    mx, mr = compare(gpu, ref)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    msg = f"{what}: max_abs={mx:.3e} (max|ref|={scale:.3e}, ratio {mx / scale:.3e}) mean_rel={mr:.3e}"
+    print(msg, flush=True)
+    assert mx <= 2e-2 * scale and mr <= 1e-2, msg
+
+
+BWD_CASES = [
+    # (B, H, Lq, q_runs, Lk, k_runs, d, causal)
+    (1, 2, 256, [(0, 256)], 256, [(0, 256)], 128, True),
+    (2, 3, 300, [(40, 137), (1000, 163)], 333, [(0, 250), (900, 83)], 128, True),
+    (1, 2, 517, [(0, 517)], 999, [(0, 999)], 64, False),
+    (1, 2, 257, [(500, 129), (2000, 128)], 700, [(300, 350), (1900, 350)], 64, True),
+    (1, 1, 96, [(0, 96)], 33, [(5, 33)], 128, False),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(BWD_CASES)))
+def test_bwd_single_block(gpu_lib, ci):
+    B, H, Lq, qr, Lk, kr, d, causal = BWD_CASES[ci]
+    banner(f"bwd case {ci}: B{B} H{H} Lq{Lq} Lk{Lk} d{d} causal={causal}")
+    dt = torch.bfloat16
+    q = seeded.gen_bhsd(300 + ci, 0, B, H, 0, Lq, d, dt, "cuda")
+    k = seeded.gen_bhsd(300 + ci, 1, B, H, 0, Lk, d, dt, "cuda")
+    v = seeded.gen_bhsd(300 + ci, 2, B, H, 0, Lk, d, dt, "cuda")
+    do = seeded.gen_bhsd(300 + ci, DOUT, B, H, 0, Lq, d, dt, "cuda")
+    scale = d ** -0.5
+    st = ring.RingState(B, H, Lq, d, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    _lib.ra_step_final(q, k, v, qr, kr, causal, scale, st.o, st.m, st.l, out, lse, init=True)
+    delta = torch.empty_like(lse)
+    _lib.ra_bwd_prep(out, do, delta)
+    dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((B, H, Lk, d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    _lib.ra_step_bwd(q, k, v, do, lse, delta, qr, kr, causal, scale, dq, dk, dv, init_dq=True, init_dkv=True)
+    torch.cuda.synchronize()
+    # delta against the exact values handed to the kernel
+    ref_delta = (out.double() * do.double()).sum(-1)
+    assert (delta.double() - ref_delta).abs().max().item() <= 1e-4 * max(1.0, ref_delta.abs().max().item())
+    qp, kp = _runs_pos(qr), _runs_pos(kr)
+    qc, kc, vc, dc = (seeded.exact_f64(t.cpu()) for t in (q, k, v, do))
+    rq, rk, rv = (np.zeros((B, H, L, d)) for L in (Lq, Lk, Lk))
+    for b in range(B):
+        for h in range(H):
+            rq[b, h], rk[b, h], rv[b, h] = oracle.attention_grads(qc[b, h], qp, kc[b, h], vc[b, h], kp, scale,
+                                                                  causal, dc[b, h])
+    for g, r, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        assert torch.isfinite(g).all(), n
+        grad_close(g.cpu().double().numpy(), r, f"bwd case {ci} {n}")
+
+
+def test_bwd_accumulates(gpu_lib):
+    banner("ra_step_bwd without the init flags adds to the accumulators")
+    B, H, L, d = 1, 2, 200, 64
+    dt = torch.bfloat16
+    q, k, v, do = (seeded.gen_bhsd(320, t, B, H, 0, L, d, dt, "cuda") for t in range(4))
+    lse = torch.full((B, H, L), 5.0, device="cuda")
+    delta = torch.full((B, H, L), 0.25, device="cuda")
+    acc = [torch.empty((B, H, L, d), dtype=torch.float32, device="cuda") for _ in range(3)]
+    _lib.ra_step_bwd(q, k, v, do, lse, delta, [(0, L)], [(0, L)], True, 0.125, *acc, init_dq=True, init_dkv=True)
+    once = [a.clone() for a in acc]
+    _lib.ra_step_bwd(q, k, v, do, lse, delta, [(0, L)], [(0, L)], True, 0.125, *acc)
+    torch.cuda.synchronize()
+    for a, o in zip(acc, once):
+        assert torch.allclose(a, 2 * o, rtol=1e-6, atol=1e-6)
+
+
+def _bwd_ring_case(w):
+    """Forward and backward of every rank of ring workload w; dK/dV accumulators
+    travel over the ranks. Returns the GPU gradients and the per-rank cases."""
+    cases = [RingCase(w, r) for r in range(w.P)]
+    dkv = None
+    dqs, dos = [], []
+    for r, case in enumerate(cases):
+        out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, r, w.causal, scale=w.scale)
+        do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, ringcase_positions(w, r), w.d, w.dtype, "cuda")
+        dq, dkv = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, r, w.causal, out, lse, do,
+                               scale=w.scale, dkv=dkv)
+        dqs.append(dq)
+        dos.append(do)
+    torch.cuda.synchronize()
+    return cases, dqs, dkv
+
+
+def ringcase_positions(w, r):
+    from ringcase import oracle_positions
+    return oracle_positions(w, r)
+
+
+def test_bwd_ring_causal_2rank_all_ranks(gpu_lib):
+    w = configs.CAUSAL_2RANK
+    banner(f"backward ring, {w.name}, both ranks; dK/dV accumulated over the ranks")
+    cases, dqs, dkv = _bwd_ring_case(w)
+    S = w.S
+    allpos = np.arange(S)
+    for b in range(w.B):
+        for h in range(w.H):
+            ex = lambda tid, rows: seeded.exact_f64(seeded.to_dtype(
+                seeded.normal_rows_at(w.wid, tid, b, h, rows, w.d), w.dtype))
+            gq, gk, gv, gdo = ex(seeded.Q, allpos), ex(seeded.K, allpos), ex(seeded.V, allpos), ex(DOUT, allpos)
+            rq, rk, rv = oracle.attention_grads(gq, allpos, gk, gv, allpos, w.scale, w.causal, gdo)
+            for r in range(w.P):
+                pos = ringcase_positions(w, r)
+                grad_close(dqs[r][b, h].cpu().double().numpy(), rq[pos], f"dq rank {r} h{h}")
+                grad_close(dkv[r][0][b, h].cpu().double().numpy(), rk[pos], f"dk block {r} h{h}")
+                grad_close(dkv[r][1][b, h].cpu().double().numpy(), rv[pos], f"dv block {r} h{h}")
+
+
+def test_bwd_ring_block_order_independent(gpu_lib):
+    w = configs.CAUSAL_2RANK
+    banner(f"backward ring, {w.name} rank 1: ring order vs reversed")
+    case = RingCase(w, 1)
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, 1, True, scale=w.scale)
+    do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, ringcase_positions(w, 1), w.d, w.dtype, "cuda")
+    dq1, kv1 = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, 1, True, out, lse, do, scale=w.scale)
+    dq2, kv2 = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, 1, True, out, lse, do, scale=w.scale,
+                            order=[0, 1])
+    torch.cuda.synchronize()
+    # dq sums the blocks in another order: equal up to fp32 rounding; dk/dv do not depend on it
+    assert torch.allclose(dq1, dq2, rtol=1e-5, atol=1e-5 * dq1.abs().max().item())
+    for (a, b), (c, e) in zip(kv1, kv2):
+        assert torch.equal(a, c) and torch.equal(b, e)
+
+
+def test_bwd_llm_32k_rank0_sampled_dq(gpu_lib):
+    w = configs.LLM_32K_CP4
+    banner(f"backward ring, {w.name} rank 0: dq on sampled rows")
+    case = RingCase(w, 0)
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, scale=w.scale)
+    qpos = ringcase_positions(w, 0)
+    do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, qpos, w.d, w.dtype, "cuda")
+    dq, dkv = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, out, lse, do, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 0)
+    allpos = np.arange(w.S)
+    gpu = dq.index_select(2, torch.as_tensor(rows, device=dq.device)).cpu().double().numpy()
+    ref = np.zeros_like(gpu)
+    for h in range(w.H):
+        ex = lambda tid, r: seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, tid, 0, h, r, w.d), w.dtype))
+        # dq_i depends on row i alone (and on every key), so a row sample is exact
+        ref[0, h], _, _ = oracle.attention_grads(ex(seeded.Q, qpos[rows]), qpos[rows], ex(seeded.K, allpos),
+                                                 ex(seeded.V, allpos), allpos, w.scale, True,
+                                                 ex(DOUT, qpos[rows]))
+    grad_close(gpu, ref, f"{w.name} dq, {rows.size} rows/head")
+    for dk, dv in dkv:
+        assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
