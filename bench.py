@@ -142,6 +142,29 @@ def time_kernel(fn, reps, warmup=3):
     return float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)]))
 
 
+def time_backward(w, rank, q, segs, kv, out, lse, reps, warmup=3):
+    """The backward pass of the same share: ra_bwd_prep and P ra_step_bwd
+    launches (dQ kernel, then dK/dV kernel), timed with HIP events on the
+    stream they run on."""
+    dev = q.device
+    do = seeded.gen_bhsd_at(w.wid, seeded.DO, w.B, w.H, positions(segs[rank]), w.d, w.dtype, dev)
+    dkv = [(torch.empty(k.shape, dtype=torch.float32, device=dev),
+            torch.empty(k.shape, dtype=torch.float32, device=dev)) for k, _ in kv]
+    box = {}
+
+    def one():
+        # fresh accumulators each pass: every block's dK/dV holds this rank's share
+        box["dq"], _ = ring.run_bwd(q, segs[rank], kv, segs, rank, w.causal, out, lse, do, scale=w.scale)
+
+    ms = time_kernel(one, reps, warmup)
+    assert torch.isfinite(box["dq"]).all(), "non-finite dq"
+    fl = 2.0 * sum(ring_flop(w, rank, segs))
+    return {"workload": f"{w.name} rank {rank}, {w.P} backward ring steps", "ms": ms,
+            "TFLOP/s": fl / ms / 1e9, "mfma_frac": fl / ms / 1e-3 / PEAK_BF16_DENSE,
+            "flop": fl, "flop_convention": "8*d per visible pair (the dV, dP, dQ and dK products); "
+            "the kernels execute 14*d (scores and dP are formed in both the dQ and the dK/dV kernel)"}
+
+
 def legs(w, q, dev, reps):
     out = {}
     # LSE merge of two normalised partials of this workload's shape (bf16)
@@ -314,6 +337,9 @@ def main():
     if not args.no_legs:
         log("[bench] legs: merge, factored spatial, factored temporal")
         rec["legs"] = legs(w, q, dev, reps=20)
+        if w.dtype == torch.bfloat16 and w.Hkv == w.H:
+            log("[bench] leg: backward ring pass")
+            rec["legs"]["backward"] = time_backward(w, args.rank, q, segs, kv, out, lse, reps=10)
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_budget:.0f} s")
         rec["cpu_baseline"] = cpu_baseline(w, args.rank, segs, args.cpu_budget)

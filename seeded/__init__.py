@@ -24,8 +24,8 @@ ROW_BLOCK = 1024
 # drawn concurrently; the values do not depend on the thread count.
 _POOL = ThreadPoolExecutor(max_workers=max(1, min(16, len(os.sched_getaffinity(0)))))
 
-# tensor ids
-Q, K, V = 0, 1, 2
+# tensor ids (DO: the upstream gradient of the attention output)
+Q, K, V, DO = 0, 1, 2, 3
 
 
 def normal_rows(wid, tid, b, h, r0, r1, d):

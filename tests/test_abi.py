@@ -167,3 +167,34 @@ def test_gqa_spans_use_the_kv_head_count(lib):
                          ctypes.byref(b), 1, 0.1, 1, o_after_one_head, ptr(4), ptr(5), None)
     assert lib.ra_step_gqa(*args(1)) == UNS
     assert lib.ra_step_gqa(*args(4)) == INV
+
+
+def step_bwd(lib, dt=1, d=128, flags=3, q=None, dout=None, lse=None, delta=None, dq=None, dk=None, dv=None):
+    a, b = _lib.segs([(0, 64)]), _lib.segs([(0, 64)])
+    pick = lambda x, i: ptr(i) if x is None else x
+    return lib.ra_step_bwd(pick(q, 0), ptr(1), ptr(2), pick(dout, 3), pick(lse, 4), pick(delta, 5), dt,
+                           1, 1, 64, 64, d, ctypes.byref(a), ctypes.byref(b), 1, 0.1, flags,
+                           pick(dq, 6), pick(dk, 7), pick(dv, 8), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dout=0), INV), (dict(lse=0), INV), (dict(delta=0), INV), (dict(dq=0), INV),
+    (dict(dk=0), INV), (dict(dv=0), INV), (dict(flags=4), INV),
+    (dict(dk=ptr(1)), INV),            # dk accumulator over the keys
+    (dict(dv=ptr(7) + 256), INV),      # dv overlapping dk
+    (dict(dq=ptr(3)), INV),            # dq over the upstream gradient
+    (dict(dt=0), UNS), (dict(d=96), UNS),
+    (dict(flags=0, d=96), UNS), (dict(flags=1, d=96), UNS), (dict(flags=2, d=96), UNS),
+])
+def test_step_bwd_rejects_bad_arguments(lib, kw, expect):
+    assert step_bwd(lib, **kw) == expect
+
+
+def test_bwd_prep_validation(lib):
+    p = lib.ra_bwd_prep
+    assert p(None, ptr(1), 1, 1, 1, 64, 128, ptr(2), None) == INV
+    assert p(ptr(0), ptr(1), 1, 1, 1, 64, 128, None, None) == INV
+    assert p(ptr(0), ptr(1), 1, 1, 1, 0, 128, ptr(2), None) == INV
+    assert p(ptr(0), ptr(1), 1, 1, 1, 64, 128, ptr(1) + 64, None) == INV  # delta inside dout
+    assert p(ptr(0), ptr(1), 0, 1, 1, 64, 128, ptr(2), None) == UNS       # fp32 inputs
+    assert p(ptr(0), ptr(1), 1, 1, 1, 64, 80, ptr(2), None) == UNS

@@ -516,7 +516,7 @@ def test_gqa_llm_32k_rank0_sampled(gpu_lib):
 
 # ---- backward ring step -------------------------------------------------------------
 
-DOUT = 3  # seeded tensor id of the upstream gradient
+DOUT = seeded.DO  # seeded tensor id of the upstream gradient
 
 
 def grad_close(gpu, ref, what):
