@@ -134,8 +134,28 @@ def _s(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _shape(name, t, want):
+    if t is not None and tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _check_step(q, k, v, o_acc, m, l, grouped=True):
+    """The sizes the C call derives from q and k must describe every buffer it touches."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    H_kv, Lk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d or H_kv < 1 or H % H_kv != 0 or (not grouped and H_kv != H):
+        raise ValueError(f"k: shape {tuple(k.shape)} does not fit q {tuple(q.shape)}")
+    _shape("v", v, k.shape)
+    _shape("o_acc", o_acc, (B, H, Lq, d))
+    _shape("m", m, (B, H, Lq))
+    _shape("l", l, (B, H, Lq))
+
+
 def ra_step(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, init=False, stream=None):
     """ra_step; with fewer K/V heads than query heads (k.shape[1] < q.shape[1]) ra_step_gqa."""
+    _check_step(q, k, v, o_acc, m, l)
     B, H, Lq, d = q.shape
     H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
@@ -151,6 +171,9 @@ def ra_step(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, init=False, st
 def ra_step_final(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, out, lse=None,
                   init=False, stream=None):
     """ra_step_final; with fewer K/V heads than query heads ra_step_final_gqa."""
+    _check_step(q, k, v, o_acc, m, l)
+    _shape("out", out, q.shape)
+    _shape("lse", lse, q.shape[:3])
     B, H, Lq, d = q.shape
     H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
@@ -167,12 +190,18 @@ def ra_step_final(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, out, lse
 
 def ra_bwd_prep(out, dout, delta, stream=None):
     B, H, L, d = out.shape
+    _shape("dout", dout, out.shape)
+    _shape("delta", delta, (B, H, L))
     _check("ra_bwd_prep", load().ra_bwd_prep(_p(out), _p(dout), _dtype(out), B, H, L, d, _p(delta),
                                              _s(stream)))
 
 
 def ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs, causal, scale, dq, dk, dv,
                 init_dq=False, init_dkv=False, stream=None):
+    _check_step(q, k, v, dq, lse, delta, grouped=False)
+    _shape("dout", dout, q.shape)
+    _shape("dk", dk, k.shape)
+    _shape("dv", dv, k.shape)
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
@@ -185,12 +214,18 @@ def ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs, causal, scale, dq, d
 
 def ra_finalize(o_acc, m, l, out, lse=None, stream=None):
     B, H, L, d = o_acc.shape
+    for n, t, want in (("m", m, (B, H, L)), ("l", l, (B, H, L)), ("out", out, o_acc.shape),
+                       ("lse", lse, (B, H, L))):
+        _shape(n, t, want)
     _check("ra_finalize", load().ra_finalize(_p(o_acc), _p(m), _p(l), B, H, L, d, _p(out),
                                              _dtype(out), _p(lse), _s(stream)))
 
 
 def ra_merge_lse(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
     B, H, L, d = o_a.shape
+    for n, t, want in (("o_b", o_b, o_a.shape), ("o_out", o_out, o_a.shape), ("lse_a", lse_a, (B, H, L)),
+                       ("lse_b", lse_b, (B, H, L)), ("lse_out", lse_out, (B, H, L))):
+        _shape(n, t, want)
     _check("ra_merge_lse", load().ra_merge_lse(_p(o_a), _p(lse_a), _p(o_b), _p(lse_b),
                                                _dtype(o_a), B, H, L, d, _p(o_out),
                                                _p(lse_out), _s(stream)))
@@ -200,6 +235,8 @@ def ra_factored_spatial(q, k, v, T, S_sp, scale, out, lse=None, stream=None):
     B, H, N, d = q.shape
     if N != T * S_sp:
         raise ValueError("q.shape[2] must equal T * S_sp")
+    for n, t, want in (("k", k, q.shape), ("v", v, q.shape), ("out", out, q.shape), ("lse", lse, (B, H, N))):
+        _shape(n, t, want)
     _check("ra_factored_spatial", load().ra_factored_spatial(
         _p(q), _p(k), _p(v), _dtype(q), B, H, T, S_sp, d, float(scale), _p(out), _p(lse), _s(stream)))
 
@@ -208,6 +245,8 @@ def ra_factored_temporal(q, k, v, T, S_sp, scale, out, lse=None, stream=None):
     B, H, N, d = q.shape
     if N != T * S_sp:
         raise ValueError("q.shape[2] must equal T * S_sp")
+    for n, t, want in (("k", k, q.shape), ("v", v, q.shape), ("out", out, q.shape), ("lse", lse, (B, H, N))):
+        _shape(n, t, want)
     _check("ra_factored_temporal", load().ra_factored_temporal(
         _p(q), _p(k), _p(v), _dtype(q), B, H, T, S_sp, d, float(scale), _p(out), _p(lse), _s(stream)))
 

@@ -198,3 +198,24 @@ def test_bwd_prep_validation(lib):
     assert p(ptr(0), ptr(1), 1, 1, 1, 64, 128, ptr(1) + 64, None) == INV  # delta inside dout
     assert p(ptr(0), ptr(1), 0, 1, 1, 64, 128, ptr(2), None) == UNS       # fp32 inputs
     assert p(ptr(0), ptr(1), 1, 1, 1, 64, 80, ptr(2), None) == UNS
+
+
+def test_binding_checks_shapes_before_calling():
+    # the binding refuses tensors whose shapes do not match what the C call
+    # would assume (CPU tensors: the check fires before any pointer is used)
+    import torch
+    q = torch.zeros((1, 4, 64, 64), dtype=torch.bfloat16)
+    k2 = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)
+    k3 = torch.zeros((1, 3, 64, 64), dtype=torch.bfloat16)
+    st = [torch.zeros((1, 4, 64, 64)), torch.zeros((1, 4, 64)), torch.zeros((1, 4, 64))]
+    with pytest.raises(ValueError):
+        _lib.ra_step(q, k3, k3, [(0, 64)], [(0, 64)], True, 0.1, *st)
+    with pytest.raises(ValueError):
+        _lib.ra_step(q, k2, k3, [(0, 64)], [(0, 64)], True, 0.1, *st)
+    with pytest.raises(ValueError):  # the backward step takes one K/V head per query head
+        _lib.ra_step_bwd(q, k2, k2, q, st[1], st[2], [(0, 64)], [(0, 64)], True, 0.1, st[0],
+                         torch.zeros((1, 2, 64, 64)), torch.zeros((1, 2, 64, 64)))
+    with pytest.raises(ValueError):
+        _lib.ra_finalize(st[0], st[1], st[2], torch.zeros((1, 4, 63, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        _lib.ra_factored_spatial(q, q, q[:, :, :32], 4, 16, 0.1, torch.empty_like(q))
