@@ -337,7 +337,7 @@ def main():
     if not args.no_legs:
         log("[bench] legs: merge, factored spatial, factored temporal")
         rec["legs"] = legs(w, q, dev, reps=20)
-        if w.dtype == torch.bfloat16 and w.Hkv == w.H:
+        if w.dtype == torch.bfloat16:
             log("[bench] leg: backward ring pass")
             rec["legs"]["backward"] = time_backward(w, args.rank, q, segs, kv, out, lse, reps=10)
     if not args.no_cpu_baseline:

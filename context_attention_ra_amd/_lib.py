@@ -55,7 +55,7 @@ _SIGS = {
                                  ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
                                  _vp, _vp, _vp, _vp, _vp, _vp]),
     "ra_bwd_prep": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
-    "ra_step_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+    "ra_step_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                            ctypes.POINTER(RaSegs), ctypes.POINTER(RaSegs), _i32, _f32, _u32,
                            _vp, _vp, _vp, _vp]),
     "ra_finalize": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
@@ -198,16 +198,16 @@ def ra_bwd_prep(out, dout, delta, stream=None):
 
 def ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs, causal, scale, dq, dk, dv,
                 init_dq=False, init_dkv=False, stream=None):
-    _check_step(q, k, v, dq, lse, delta, grouped=False)
+    _check_step(q, k, v, dq, lse, delta)
     _shape("dout", dout, q.shape)
     _shape("dk", dk, k.shape)
     _shape("dv", dv, k.shape)
     B, H, Lq, d = q.shape
-    Lk = k.shape[2]
+    H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
     flags = (RA_STEP_INIT if init_dq else 0) | (RA_BWD_KV_INIT if init_dkv else 0)
     _check("ra_step_bwd", load().ra_step_bwd(
-        _p(q), _p(k), _p(v), _p(dout), _p(lse), _p(delta), _dtype(q), B, H, Lq, Lk, d,
+        _p(q), _p(k), _p(v), _p(dout), _p(lse), _p(delta), _dtype(q), B, H, H_kv, Lq, Lk, d,
         ctypes.byref(qs), ctypes.byref(ks), RA_MASK_CAUSAL if causal else RA_MASK_NONE,
         float(scale), flags, _p(dq), _p(dk), _p(dv), _s(stream)))
 

@@ -21,6 +21,10 @@
 // * bwd_dkdv: each wave owns 32 key rows and streams 64-row Q/dO tiles:
 //   S = Q K^T and dP = dO V^T (every lane owns one key; the per-row lse and
 //   delta of the tile come from LDS), then dV^T += dO^T P and dK^T += Q^T dS.
+// With fewer K/V heads than query heads (G consecutive query heads per K/V
+// head), the dQ kernel reads K/V slice p / G and the dK/dV kernel walks the
+// Q/dO tiles of all G query heads of its K/V head, so their contributions sum
+// in one accumulator.
 // Both recompute S and dP, so the matrix cores run 14*d FLOP per visible
 // pair against the 8*d of the four products the gradients need.
 // The LDS tile layout, the operand reads and the key permutation inside each
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
     int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, float scale,
-    int32_t init, float* __restrict__ dQ, int32_t nqt, int32_t per_xcd) {
+    int32_t init, float* __restrict__ dQ, int32_t nqt, int32_t per_xcd, int32_t group) {
   using L = BLay<D>;
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
@@ -221,8 +225,9 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     return;
   }
 
-  const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + (size_t)prob * Lk * D, Lk, D);
-  const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + (size_t)prob * Lk * D, Lk, D);
+  const size_t kvbase = (size_t)(prob / group) * Lk * D;  // the K/V head of this query head
+  const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + kvbase, Lk, D);
+  const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + kvbase, Lk, D);
   auto fetch = [&](int32_t n) {
     char* st = smem + (n & 1) * L::STAGE;
     const int32_t r0 = tile_row0(tr, n);
@@ -315,14 +320,15 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
     int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, float scale,
-    int32_t init, float* __restrict__ dK, float* __restrict__ dV, int32_t nkt, int32_t per_xcd) {
+    int32_t init, float* __restrict__ dK, float* __restrict__ dV, int32_t nkt, int32_t per_xcd,
+    int32_t group) {
   using L = BLay<D>;
   constexpr int KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int32_t logical = xcd_logical(per_xcd);
-  if (logical >= nb * nkt) return;
-  const int32_t prob = logical / nkt;
+  if (logical >= nb * nkt) return;  // nb counts K/V slices here
+  const int32_t prob = logical / nkt;  // K/V slice; its query slices are prob*group ..
   const int32_t k0 = (logical - prob * nkt) * kOwn;
 
   const int32_t w_r0 = k0 + 32 * w;
@@ -346,6 +352,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
   const size_t kb = (size_t)prob * Lk;
   float* dkp = dK + (kb + krow) * D + 4 * h;
   float* dvp = dV + (kb + krow) * D + 4 * h;
+  // the stream: tr.n tiles of each of the group's query heads in turn
+  const int32_t ntiles = tr.n * group;
   if (tr.n == 0) {
     if (init && kvalid) {
 #pragma unroll
@@ -359,15 +367,16 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
     return;
   }
 
-  const size_t rbase = (size_t)prob * Lq;
-  const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(Q + rbase * D, Lq, D);
-  const __amdgpu_buffer_rsrc_t drs = slice_rsrc(dO + rbase * D, Lq, D);
+  // query slice and tile of stream tile m
+  auto qslice = [&](int32_t m) { return (size_t)prob * group + m / tr.n; };
+  auto qtile = [&](int32_t m) { return tile_row0(tr, m % tr.n); };
   // lse (log2 units) and delta of the tile's rows: thread i < 64 brings the
   // lse of row i, thread 64 + i its delta; rows past the end get lse = +inf
   // (so P = 0) and delta = 0
   float rowv = 0.f;
   auto fetch_rowv = [&](int32_t n) {
-    const int32_t r = tile_row0(tr, n) + (tid & 63);
+    const size_t rbase = qslice(n) * Lq;
+    const int32_t r = qtile(n) + (tid & 63);
     if (tid < 64) {
       const float x = r < Lq ? Lse[rbase + r] : kNegInf;
       rowv = x != kNegInf ? x * kLog2e : __builtin_inff();
@@ -380,9 +389,10 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
   };
   auto fetch = [&](int32_t n) {
     char* st = smem + (n & 1) * L::STAGE;
-    const int32_t r0 = tile_row0(tr, n);
-    load_tile<D>(qrs, st, r0, w, lane);
-    load_tile<D>(drs, st + L::TBYTES, r0, w, lane);
+    const size_t rbase = qslice(n) * Lq;
+    const int32_t r0 = qtile(n);
+    load_tile<D>(slice_rsrc(Q + rbase * D, Lq, D), st, r0, w, lane);
+    load_tile<D>(slice_rsrc(dO + rbase * D, Lq, D), st + L::TBYTES, r0, w, lane);
   };
   fetch_rowv(0);
   fetch(0);
@@ -403,8 +413,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   store_rowv(0);
   __syncthreads();
-  for (int32_t n = 0; n < tr.n; ++n) {
-    if (n + 1 < tr.n) {
+  for (int32_t n = 0; n < ntiles; ++n) {
+    if (n + 1 < ntiles) {
       fetch_rowv(n + 1);
       fetch(n + 1);
     }
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
     const char* dt = qt + L::TBYTES;
     const float* lsev = (const float*)(qt + 2 * L::TBYTES);
     const float* dltv = lsev + kT;
-    const int32_t qt0 = tile_row0(tr, n);
+    const int32_t qt0 = qtile(n);
     bool need_mask = false;
     if (CAUSAL) {
       int32_t qlo, qhi;
@@ -459,7 +469,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
       }
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    if (n + 1 < tr.n) store_rowv(n + 1);
+    if (n + 1 < ntiles) store_rowv(n + 1);
     __syncthreads();
   }
   if (!kvalid) return;
@@ -506,18 +516,19 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   const int32_t nqt = (a.Lq + kOwn - 1) / kOwn, nkt = (a.Lk + kOwn - 1) / kOwn;
+  const int32_t nkv = a.nb / a.group;
   const int32_t pq = (int32_t)(((int64_t)a.nb * nqt + kXcdsB - 1) / kXcdsB);
-  const int32_t pk = (int32_t)(((int64_t)a.nb * nkt + kXcdsB - 1) / kXcdsB);
+  const int32_t pk = (int32_t)(((int64_t)nkv * nkt + kXcdsB - 1) / kXcdsB);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(kXcdsB * pq), dim3(kBThreads), 0, st,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
                      a.lse, a.delta, a.nb, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
-                     (int32_t)a.init_dq, a.dq, nqt, pq);
+                     (int32_t)a.init_dq, a.dq, nqt, pq, a.group);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(kXcdsB * pk), dim3(kBThreads), 0, st,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
-                     a.lse, a.delta, a.nb, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
-                     (int32_t)a.init_dkv, a.dk, a.dv, nkt, pk);
+                     a.lse, a.delta, nkv, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
+                     (int32_t)a.init_dkv, a.dk, a.dv, nkt, pk, a.group);
   return hipGetLastError();
 }
 

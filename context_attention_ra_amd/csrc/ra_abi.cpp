@@ -181,7 +181,7 @@ ra_status ra_bwd_prep(const void* out, const void* dout, ra_dtype dt, int32_t B,
 
 ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, const float* delta, ra_dtype dt, int32_t B, int32_t H,
-                      int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
+                      int32_t H_kv, int32_t Lq, int32_t Lk, int32_t d, const ra_segs* q_segs,
                       const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
                       float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream) {
   if (!dout || !lse || !delta || !dq_acc || !dk_acc || !dv_acc) return RA_ERR_INVALID_ARG;
@@ -189,15 +189,15 @@ ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* d
   // the forward checks cover q, k, v, the sizes, segments, mask and scale; dq_acc
   // and the two per-row vectors take the places of o_acc, m and l
   ra::StepArgs sa;
-  const ra_status st = step_args(q, k, v, dt, B, H, H, Lq, Lk, d, q_segs, kv_segs, mask, scale,
+  const ra_status st = step_args(q, k, v, dt, B, H, H_kv, Lq, Lk, d, q_segs, kv_segs, mask, scale,
                                  flags & RA_STEP_INIT, dq_acc, (float*)lse, (float*)delta, &sa);
   if (st != RA_OK) return st;
   if (!aligned(dout, 16) || !aligned(dk_acc, 16) || !aligned(dv_acc, 16)) return RA_ERR_INVALID_ARG;
-  const size_t nb = (size_t)B * H, es = esize(dt);
-  const Range in[] = {span(q, nb * Lq * d * es), span(k, nb * Lk * d * es), span(v, nb * Lk * d * es),
+  const size_t nb = (size_t)B * H, nkv = (size_t)B * H_kv, es = esize(dt);
+  const Range in[] = {span(q, nb * Lq * d * es), span(k, nkv * Lk * d * es), span(v, nkv * Lk * d * es),
                       span(dout, nb * Lq * d * es), span(lse, nb * Lq * 4), span(delta, nb * Lq * 4)};
-  const Range acc[] = {span(dq_acc, nb * Lq * d * 4), span(dk_acc, nb * Lk * d * 4),
-                       span(dv_acc, nb * Lk * d * 4)};
+  const Range acc[] = {span(dq_acc, nb * Lq * d * 4), span(dk_acc, nkv * Lk * d * 4),
+                       span(dv_acc, nkv * Lk * d * 4)};
   for (int i = 0; i < 3; ++i) {
     for (Range x : in)
       if (overlap(acc[i], x)) return RA_ERR_INVALID_ARG;
@@ -216,6 +216,7 @@ ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* d
   a.Lq = Lq;
   a.Lk = Lk;
   a.d = d;
+  a.group = sa.group;
   a.qs = sa.qs;
   a.ks = sa.ks;
   a.causal = sa.causal;

@@ -9,8 +9,9 @@
 
 namespace ra {
 
-// One backward step: `nb` (batch*head) slices, Lq local query rows against an
-// Lk-row K/V block, with the final forward lse and delta = <dO, O> per row.
+// One backward step: `nb` (batch*head) query slices of Lq local rows against
+// nb / group K/V slices of an Lk-row block (query slice p reads K/V slice
+// p / group), with the final forward lse and delta = <dO, O> per query row.
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -19,6 +20,7 @@ struct BwdArgs {
   const float* lse;
   const float* delta;
   int32_t nb, Lq, Lk, d;
+  int32_t group;  // query heads per K/V head
   HostSegs qs, ks;
   bool causal;
   bool init_dq;   // dq starts at zero (not read)

@@ -202,7 +202,11 @@ ra_status ra_bwd_prep(const void* out, const void* dout, ra_dtype dt, int32_t B,
  * Summed over the P blocks (dq) and over the P ranks' queries (dk, dv) these
  * are the exact gradients of the attention, whatever the order.
  * q, dout  [B,H,Lq,d] local queries and the upstream gradient of their output
- * k, v     [B,H,Lk,d] the block held at this step
+ * k, v     [B,H_kv,Lk,d] the block held at this step; H_kv K/V heads as for
+ *          ra_step_gqa (query head h reads K/V head h / (H / H_kv); H_kv == H
+ *          is one K/V head per query head); the dk_acc and dv_acc rows of a
+ *          K/V head sum the contributions of the H / H_kv query heads that
+ *          share it
  * lse      [B,H,Lq] fp32, the final forward lse of the local queries
  *          (ra_step_final / ra_finalize); -inf rows contribute nothing
  * delta    [B,H,Lq] fp32 from ra_bwd_prep
@@ -210,16 +214,16 @@ ra_status ra_bwd_prep(const void* out, const void* dout, ra_dtype dt, int32_t B,
  *          the forward pass)
  * flags    0, RA_STEP_INIT (dq_acc starts at zero), RA_BWD_KV_INIT (dk_acc,
  *          dv_acc start at zero), or both
- * dq_acc   [B,H,Lq,d] fp32 in/out; dk_acc, dv_acc [B,H,Lk,d] fp32 in/out
+ * dq_acc   [B,H,Lq,d] fp32 in/out; dk_acc, dv_acc [B,H_kv,Lk,d] fp32 in/out
  * dt must be RA_BF16 (inputs bf16, products on the matrix cores, fp32
  * accumulation). The two kernels run one after the other on `stream`.
- * Errors: those of ra_step, RA_ERR_INVALID_ARG for a null dout, lse, delta or
+ * Errors: those of ra_step_gqa, RA_ERR_INVALID_ARG for a null dout, lse, delta or
  *   accumulator, unknown flags, or an accumulator overlapping an input or
  *   another accumulator; RA_ERR_UNSUPPORTED for dt != RA_BF16.
  */
 ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, const float* delta, ra_dtype dt,
-                      int32_t B, int32_t H, int32_t Lq, int32_t Lk, int32_t d,
+                      int32_t B, int32_t H, int32_t H_kv, int32_t Lq, int32_t Lk, int32_t d,
                       const ra_segs* q_segs, const ra_segs* kv_segs, ra_mask mask,
                       float scale, uint32_t flags, float* dq_acc, float* dk_acc,
                       float* dv_acc, hipStream_t stream);

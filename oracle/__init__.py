@@ -28,6 +28,7 @@ from .attention import (  # noqa: F401
     factored_spatial,
     factored_temporal,
     grouped_attention,
+    grouped_attention_grads,
     merge_lse,
 )
 from .layout import (  # noqa: F401

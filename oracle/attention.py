@@ -139,6 +139,30 @@ def grouped_attention(q, q_pos, k, v, k_pos, scale, causal):
     return o, lse
 
 
+def grouped_attention_grads(q, q_pos, k, v, k_pos, scale, causal, do):
+    """Gradients of ``grouped_attention``: query head h reads K/V head
+    floor(h / G), so each K/V head's gradient is the sum of the gradients of
+    the G query heads that share it (the chain rule for a shared input).
+
+    q, do (H, n, d); k, v (H_kv, S, d).
+    returns (dq (H, n, d), dk (H_kv, S, d), dv (H_kv, S, d)) in fp64
+    """
+    H, n, d = np.shape(q)
+    H_kv = np.shape(k)[0]
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError("the query head count must be a multiple of the K/V head count")
+    G = H // H_kv
+    dq = np.zeros((H, n, d), dtype=np.float64)
+    dk = np.zeros(np.shape(k), dtype=np.float64)
+    dv = np.zeros(np.shape(v), dtype=np.float64)
+    for h in range(H):
+        a, b, c = attention_grads(q[h], q_pos, k[h // G], v[h // G], k_pos, scale, causal, do[h])
+        dq[h] = a
+        dk[h // G] += b
+        dv[h // G] += c
+    return dq, dk, dv
+
+
 def factored_spatial(q, k, v, T, S_sp, scale):
     """Spatial attention of a frame-major video token sequence.
 

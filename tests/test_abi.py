@@ -169,11 +169,12 @@ def test_gqa_spans_use_the_kv_head_count(lib):
     assert lib.ra_step_gqa(*args(4)) == INV
 
 
-def step_bwd(lib, dt=1, d=128, flags=3, q=None, dout=None, lse=None, delta=None, dq=None, dk=None, dv=None):
+def step_bwd(lib, dt=1, d=128, flags=3, q=None, dout=None, lse=None, delta=None, dq=None, dk=None, dv=None,
+             H=1, H_kv=1):
     a, b = _lib.segs([(0, 64)]), _lib.segs([(0, 64)])
     pick = lambda x, i: ptr(i) if x is None else x
     return lib.ra_step_bwd(pick(q, 0), ptr(1), ptr(2), pick(dout, 3), pick(lse, 4), pick(delta, 5), dt,
-                           1, 1, 64, 64, d, ctypes.byref(a), ctypes.byref(b), 1, 0.1, flags,
+                           1, H, H_kv, 64, 64, d, ctypes.byref(a), ctypes.byref(b), 1, 0.1, flags,
                            pick(dq, 6), pick(dk, 7), pick(dv, 8), None)
 
 
@@ -185,6 +186,7 @@ def step_bwd(lib, dt=1, d=128, flags=3, q=None, dout=None, lse=None, delta=None,
     (dict(dq=ptr(3)), INV),            # dq over the upstream gradient
     (dict(dt=0), UNS), (dict(d=96), UNS),
     (dict(flags=0, d=96), UNS), (dict(flags=1, d=96), UNS), (dict(flags=2, d=96), UNS),
+    (dict(H=4, H_kv=3), INV), (dict(H=4, H_kv=0), INV), (dict(H=4, H_kv=2, d=96), UNS),
 ])
 def test_step_bwd_rejects_bad_arguments(lib, kw, expect):
     assert step_bwd(lib, **kw) == expect
@@ -212,9 +214,9 @@ def test_binding_checks_shapes_before_calling():
         _lib.ra_step(q, k3, k3, [(0, 64)], [(0, 64)], True, 0.1, *st)
     with pytest.raises(ValueError):
         _lib.ra_step(q, k2, k3, [(0, 64)], [(0, 64)], True, 0.1, *st)
-    with pytest.raises(ValueError):  # the backward step takes one K/V head per query head
+    with pytest.raises(ValueError):  # dk/dv accumulators shaped like the K/V block
         _lib.ra_step_bwd(q, k2, k2, q, st[1], st[2], [(0, 64)], [(0, 64)], True, 0.1, st[0],
-                         torch.zeros((1, 2, 64, 64)), torch.zeros((1, 2, 64, 64)))
+                         torch.zeros((1, 4, 64, 64)), torch.zeros((1, 4, 64, 64)))
     with pytest.raises(ValueError):
         _lib.ra_finalize(st[0], st[1], st[2], torch.zeros((1, 4, 63, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError):

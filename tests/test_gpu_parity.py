@@ -670,3 +670,50 @@ def test_bwd_llm_32k_rank0_sampled_dq(gpu_lib):
     grad_close(gpu, ref, f"{w.name} dq, {rows.size} rows/head")
     for dk, dv in dkv:
         assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2])  # the bf16 cases (the backward step is bf16 only)
+def test_bwd_gqa_single_block(gpu_lib, ci):
+    B, H, Hkv, Lq, qr, Lk, kr, d, causal, dt = GQA_CASES[ci]
+    banner(f"bwd gqa case {ci}: B{B} H{H} H_kv{Hkv} Lq{Lq} Lk{Lk} d{d} causal={causal}")
+    q, k, v = _gqa_inputs(ci, B, H, Hkv, Lq, Lk, d, dt)
+    do = seeded.gen_bhsd(200 + ci, DOUT, B, H, 0, Lq, d, dt, "cuda")
+    scale = d ** -0.5
+    st = ring.RingState(B, H, Lq, d, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    _lib.ra_step_final(q, k, v, qr, kr, causal, scale, st.o, st.m, st.l, out, lse, init=True)
+    delta = torch.empty_like(lse)
+    _lib.ra_bwd_prep(out, do, delta)
+    dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((B, Hkv, Lk, d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    _lib.ra_step_bwd(q, k, v, do, lse, delta, qr, kr, causal, scale, dq, dk, dv, init_dq=True, init_dkv=True)
+    torch.cuda.synchronize()
+    qp, kp = _runs_pos(qr), _runs_pos(kr)
+    qc, kc, vc, dc = (seeded.exact_f64(t.cpu()) for t in (q, k, v, do))
+    rq, rk, rv = np.zeros((B, H, Lq, d)), np.zeros((B, Hkv, Lk, d)), np.zeros((B, Hkv, Lk, d))
+    for b in range(B):
+        rq[b], rk[b], rv[b] = oracle.grouped_attention_grads(qc[b], qp, kc[b], vc[b], kp, scale, causal, dc[b])
+    for g, r, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        grad_close(g.cpu().double().numpy(), r, f"bwd gqa case {ci} {n}")
+
+
+def test_bwd_gqa_ring_causal_2rank_all_ranks(gpu_lib):
+    w = configs.CAUSAL_2RANK_GQA
+    banner(f"backward ring, {w.name} (H={w.H}, H_kv={w.Hkv}), both ranks")
+    cases, dqs, dkv = _bwd_ring_case(w)
+    allpos = np.arange(w.S)
+    for b in range(w.B):
+        ex = lambda tid, h: seeded.exact_f64(seeded.to_dtype(
+            seeded.normal_rows_at(w.wid, tid, b, h, allpos, w.d), w.dtype))
+        gq = np.stack([ex(seeded.Q, h) for h in range(w.H)])
+        gdo = np.stack([ex(DOUT, h) for h in range(w.H)])
+        gk = np.stack([ex(seeded.K, h) for h in range(w.Hkv)])
+        gv = np.stack([ex(seeded.V, h) for h in range(w.Hkv)])
+        rq, rk, rv = oracle.grouped_attention_grads(gq, allpos, gk, gv, allpos, w.scale, w.causal, gdo)
+        for r in range(w.P):
+            pos = ringcase_positions(w, r)
+            grad_close(dqs[r][b].cpu().double().numpy(), rq[:, pos], f"dq rank {r}")
+            grad_close(dkv[r][0][b].cpu().double().numpy(), rk[:, pos], f"dk block {r}")
+            grad_close(dkv[r][1][b].cpu().double().numpy(), rv[:, pos], f"dv block {r}")

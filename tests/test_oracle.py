@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from oracle import (attention_grads, attention_rows, factored_spatial, factored_temporal,
-                    grouped_attention, merge_lse)
+                    grouped_attention, grouped_attention_grads, merge_lse)
 
 
 def brute_attention(q, q_pos, k, v, k_pos, scale, causal):
@@ -273,6 +273,20 @@ def test_grouped_with_one_group_per_head_is_per_head_attention():
                                  kp.tolist(), 0.4, True)
         np.testing.assert_allclose(o[h], bo, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(lse[h], bl, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_grads_match_torch_autograd_gqa_float64(causal):
+    # library routine: autograd through SDPA with enable_gqa (shared K/V heads)
+    H, H_kv, L, d = 6, 2, 24, 8
+    q, k, v, do = rnd(74, H, L, d), rnd(75, H_kv, L, d), rnd(76, H_kv, L, d), rnd(77, H, L, d)
+    pos = np.arange(L)
+    dq, dk, dv = grouped_attention_grads(q, pos, k, v, pos, 1.0 / math.sqrt(d), causal, do)
+    tq, tk, tv = (torch.from_numpy(a)[None].requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, enable_gqa=True)
+    out.backward(torch.from_numpy(do)[None])
+    for mine, ref in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, ref.grad[0].numpy(), rtol=1e-10, atol=1e-12)
 
 
 def test_grouped_rejects_heads_that_do_not_divide():
