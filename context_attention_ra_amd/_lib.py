@@ -23,7 +23,7 @@ RA_BWD_KV_INIT = 2
 
 # every symbol include/ra.h declares
 EXPORTS = ("ra_step", "ra_finalize", "ra_step_final", "ra_step_gqa", "ra_step_final_gqa",
-           "ra_bwd_prep", "ra_step_bwd",
+           "ra_bwd_prep", "ra_step_bwd", "ra_copy_rows",
            "ra_merge_lse", "ra_factored_spatial",
            "ra_factored_temporal", "ra_kv_pass", "ra_status_string",
            "ra_last_hip_error", "ra_version")
@@ -68,6 +68,8 @@ _SIGS = {
     "ra_factored_temporal": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                     _vp, _vp, _vp]),
     "ra_kv_pass": (_i32, [_vp, _vp, _vp, _vp, _sz, _vp]),
+    "ra_copy_rows": (_i32, [_vp, ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64,
+                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp]),
     "ra_status_string": (ctypes.c_char_p, [_i32]),
     "ra_last_hip_error": (_i32, []),
     "ra_version": (_i32, []),
@@ -258,3 +260,24 @@ def ra_kv_pass(k_src, v_src, k_dst, v_dst, stream=None):
             raise ValueError("ra_kv_pass: all four buffers must have the same size")
     _check("ra_kv_pass", load().ra_kv_pass(_p(k_src), _p(v_src), _p(k_dst), _p(v_dst),
                                            nbytes, _s(stream)))
+
+
+def ra_copy_rows(src, src_row0, dst, dst_row0, nrows, src_slice0=0, dst_slice0=0, nslices=None,
+                 stream=None):
+    """Rows [src_row0, +nrows) of slices src_slice0.. of a [..., rows, d] tensor into rows
+    [dst_row0, +nrows) of slices dst_slice0.. of another (slices = the flattened leading dims)."""
+    if src.dtype != dst.dtype or src.shape[-1] != dst.shape[-1]:
+        raise ValueError("ra_copy_rows: source and destination need the same dtype and row width")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("tensors passed to libra must be contiguous")
+    sr, dr = src.shape[-2], dst.shape[-2]
+    ns, nd = src.numel() // (sr * src.shape[-1]), dst.numel() // (dr * dst.shape[-1])
+    if nslices is None:
+        nslices = ns - src_slice0
+    if src_slice0 < 0 or dst_slice0 < 0 or src_slice0 + nslices > ns or dst_slice0 + nslices > nd:
+        raise ValueError("ra_copy_rows: slice range outside a tensor")
+    row_bytes = src.shape[-1] * src.element_size()
+    sp = src.data_ptr() + src_slice0 * sr * row_bytes
+    dp = dst.data_ptr() + dst_slice0 * dr * row_bytes
+    _check("ra_copy_rows", load().ra_copy_rows(sp, sr, src_row0, dp, dr, dst_row0, nslices, nrows,
+                                               row_bytes, _s(stream)))

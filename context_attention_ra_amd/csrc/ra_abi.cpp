@@ -328,6 +328,24 @@ ra_status ra_kv_pass(const void* k_src, const void* v_src, void* k_dst, void* v_
   return hip_fail(err);
 }
 
+ra_status ra_copy_rows(const void* src, int64_t src_slice_rows, int64_t src_row0, void* dst,
+                       int64_t dst_slice_rows, int64_t dst_row0, int64_t nslices, int64_t nrows,
+                       int64_t row_bytes, hipStream_t stream) {
+  if (nrows == 0) return RA_OK;
+  if (!src || !dst || nslices <= 0 || nrows < 0 || row_bytes <= 0) return RA_ERR_INVALID_ARG;
+  if (src_row0 < 0 || dst_row0 < 0 || src_row0 + nrows > src_slice_rows ||
+      dst_row0 + nrows > dst_slice_rows)
+    return RA_ERR_INVALID_ARG;
+  const size_t sp = (size_t)src_slice_rows * row_bytes, dp = (size_t)dst_slice_rows * row_bytes;
+  const Range rs = span((const char*)src + src_row0 * row_bytes, sp * (nslices - 1) + nrows * row_bytes);
+  const Range rd = span((const char*)dst + dst_row0 * row_bytes, dp * (nslices - 1) + nrows * row_bytes);
+  if (overlap(rs, rd)) return RA_ERR_INVALID_ARG;
+  return hip_fail(hipMemcpy2DAsync((char*)dst + dst_row0 * row_bytes, dp,
+                                   (const char*)src + src_row0 * row_bytes, sp,
+                                   (size_t)nrows * row_bytes, (size_t)nslices,
+                                   hipMemcpyDeviceToDevice, stream));
+}
+
 const char* ra_status_string(ra_status s) {
   switch (s) {
     case RA_OK: return "RA_OK";

@@ -283,6 +283,25 @@ ra_status ra_factored_temporal(const void* q, const void* k, const void* v, ra_d
 ra_status ra_kv_pass(const void* k_src, const void* v_src, void* k_dst, void* v_dst,
                      size_t bytes, hipStream_t stream);
 
+/*
+ * ra_copy_rows — the exchanges of the two alternatives to the ring that the
+ * k8ai page names ("An alternative: all-to-all on heads"; gathering every K/V
+ * block), simulated on one GPU: an asynchronous strided device-to-device copy
+ * of `nrows` consecutive rows from each of `nslices` slices of a source
+ * tensor into the same number of slices of a destination tensor.
+ *   dst[s][dst_row0 + i] = src[s][src_row0 + i] for s < nslices, i < nrows
+ * where slice s of src starts at src + s * src_slice_rows * row_bytes (and
+ * likewise for dst). row_bytes is the size of one row (d * element size).
+ * Used to place blocks at their global positions (all-gather) and to move a
+ * head group between sequence-sharded and head-sharded layouts (all-to-all).
+ * Errors: RA_ERR_INVALID_ARG for null pointers, nslices / nrows / row_bytes
+ *   <= 0, a row range outside its slice, or source and destination ranges
+ *   that overlap. nrows == 0 is a no-op.
+ */
+ra_status ra_copy_rows(const void* src, int64_t src_slice_rows, int64_t src_row0,
+                       void* dst, int64_t dst_slice_rows, int64_t dst_row0,
+                       int64_t nslices, int64_t nrows, int64_t row_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* ra_status_string(ra_status s);
 

@@ -221,3 +221,23 @@ def test_binding_checks_shapes_before_calling():
         _lib.ra_finalize(st[0], st[1], st[2], torch.zeros((1, 4, 63, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         _lib.ra_factored_spatial(q, q, q[:, :, :32], 4, 16, 0.1, torch.empty_like(q))
+
+
+def test_copy_rows_validation(lib):
+    c = lib.ra_copy_rows
+    assert c(ptr(0), 64, 0, ptr(1), 64, 0, 4, 0, 256, None) == _lib.RA_OK  # no rows: no-op
+    assert c(None, 64, 0, ptr(1), 64, 0, 4, 8, 256, None) == INV
+    assert c(ptr(0), 64, 0, ptr(1), 64, 0, 0, 8, 256, None) == INV          # no slices
+    assert c(ptr(0), 64, 60, ptr(1), 64, 0, 4, 8, 256, None) == INV         # past the source slice
+    assert c(ptr(0), 64, 0, ptr(1), 64, 60, 4, 8, 256, None) == INV         # past the destination slice
+    assert c(ptr(0), 64, -1, ptr(1), 64, 0, 4, 8, 256, None) == INV
+    assert c(ptr(0), 64, 0, ptr(0) + 256 * 8, 64, 0, 4, 8, 256, None) == INV  # overlapping ranges
+
+
+def test_variants_refuse_segments_that_do_not_tile_the_sequence():
+    from context_attention_ra_amd import variants
+    with pytest.raises(ValueError):
+        variants._global_length([[(0, 10)], [(12, 10)]])
+    with pytest.raises(ValueError):
+        variants._global_length([[(0, 10)], [(5, 10)]])
+    assert variants._global_length([[(0, 4), (12, 4)], [(4, 8)]]) == 16

@@ -717,3 +717,54 @@ def test_bwd_gqa_ring_causal_2rank_all_ranks(gpu_lib):
             grad_close(dqs[r][b].cpu().double().numpy(), rq[:, pos], f"dq rank {r}")
             grad_close(dkv[r][0][b].cpu().double().numpy(), rk[:, pos], f"dk block {r}")
             grad_close(dkv[r][1][b].cpu().double().numpy(), rv[:, pos], f"dv block {r}")
+
+
+# ---- the alternatives to the ring: all-gather and all-to-all on heads ------------------
+
+from context_attention_ra_amd import variants  # noqa: E402
+
+
+@pytest.mark.parametrize("wname", ["causal-bf16-4k-cp2", "causal-bf16-4k-cp2-gqa4"])
+def test_allgather_every_rank(gpu_lib, wname):
+    w = configs.RING_WORKLOADS[wname]
+    for rank in range(w.P):
+        banner(f"all-gather variant, {w.name} rank {rank}")
+        case = RingCase(w, rank)
+        out, lse = variants.run_allgather(case.q, case.q_segs, case.kv, case.kv_segs, w.causal, scale=w.scale)
+        torch.cuda.synchronize()
+        ro, rl = case.expected()
+        assert_close(out.float().cpu().double().numpy(), ro, lse.cpu().double().numpy(), rl, w.dtype,
+                     f"all-gather {w.name} r{rank}")
+
+
+@pytest.mark.parametrize("wname", ["causal-bf16-4k-cp2", "causal-bf16-4k-cp2-gqa4"])
+def test_head_all_to_all_every_group(gpu_lib, wname):
+    w = configs.RING_WORKLOADS[wname]
+    cases = [RingCase(w, r) for r in range(w.P)]
+    segs = [c.q_segs for c in cases]
+    qb = [c.q for c in cases]
+    kvb = cases[0].kv  # every rank's K/V block, as each case holds them all
+    hg = w.H // w.P
+    outs = [torch.empty_like(c.q) for c in cases]
+    for g in range(w.P):
+        banner(f"all-to-all on heads, {w.name} group {g} (heads {g * hg}..{(g + 1) * hg - 1})")
+        out, lse = variants.run_head_group(qb, kvb, segs, g, w.causal, scale=w.scale)
+        variants.group_to_ranks(out, g, w.P, segs, outs)
+        torch.cuda.synchronize()
+        # head group g at every position, against the oracle at positions 0..S-1
+        allpos = np.arange(w.S)
+        G = w.H // w.Hkv
+        for j in range(hg):
+            h = g * hg + j
+            ex = lambda tid, hh: seeded.exact_f64(seeded.to_dtype(
+                seeded.normal_rows_at(w.wid, tid, 0, hh, allpos, w.d), w.dtype))
+            ro, rl = oracle.grouped_attention(ex(seeded.Q, h)[None], allpos, ex(seeded.K, h // G)[None],
+                                              ex(seeded.V, h // G)[None], allpos, w.scale, w.causal)
+            assert_close(out[0, j].float().cpu().double().numpy(), ro[0], lse[0, j].cpu().double().numpy(),
+                         rl[0], w.dtype, f"group {g} head {h}")
+    # the all-to-all back gives every rank its sequence-split output of all heads
+    for r, c in enumerate(cases):
+        ro, rl = c.expected()
+        mx, mr = compare(outs[r].float().cpu().double().numpy(), ro)
+        print(f"rank {r} reassembled: max_abs={mx:.3e} mean_rel={mr:.3e}", flush=True)
+        assert mx <= 2e-2 and mr <= 1e-2
