@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import seeded  # noqa: E402
-from context_attention_ra_amd import _lib, configs, layout, ring, sizing  # noqa: E402
+from context_attention_ra_amd import _lib, configs, layout, ring, sizing, variants  # noqa: E402
 
 PEAK_BF16_DENSE = 2.5e15    # MI355X bf16 dense matrix-core FLOP/s (published)
 PEAK_HBM = 8.0e12           # MI355X HBM3E bytes/s (published)
@@ -163,6 +163,31 @@ def time_backward(w, rank, q, segs, kv, out, lse, reps, warmup=3):
             "TFLOP/s": fl / ms / 1e9, "mfma_frac": fl / ms / 1e-3 / PEAK_BF16_DENSE,
             "flop": fl, "flop_convention": "8*d per visible pair (the dV, dP, dQ and dK products); "
             "the kernels execute 14*d (scores and dP are formed in both the dQ and the dK/dV kernel)"}
+
+
+def time_variants(w, rank, q, segs, kv, reps, warmup=2):
+    """The alternatives to the ring on the same workload: the rank's queries
+    against the all-gathered K/V (gather copies plus one step launch), and
+    head group `rank` of the all-to-all on heads (the re-layout copies plus
+    one step launch over the whole sequence). Same algorithmic FLOP per rank
+    as the ring pass."""
+    dev = q.device
+    res = {}
+    fl = sum(ring_flop(w, rank, segs))
+    ms = time_kernel(lambda: variants.run_allgather(q, segs[rank], kv, segs, w.causal, scale=w.scale),
+                     reps, warmup)
+    res["all_gather"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "flop": fl}
+    if w.H % w.P == 0 and w.Hkv % w.P == 0:
+        qb = [q if t == rank else seeded.gen_bhsd_at(w.wid, seeded.Q, w.B, w.H, positions(segs[t]), w.d,
+                                                     w.dtype, dev) for t in range(w.P)]
+        full = [(0, w.S)]
+        flh = sizing.attention_flop(sizing.pairs(full, full, w.causal), w.d, w.B * (w.H // w.P))
+        ms = time_kernel(lambda: variants.run_head_group(qb, kv, segs, rank, w.causal, scale=w.scale),
+                         reps, warmup)
+        res["all_to_all_heads"] = {"ms": ms, "TFLOP/s": flh / ms / 1e9, "flop": flh,
+                                   "heads": f"{w.H // w.P} of {w.H} over all {w.S} positions"}
+    res["workload"] = f"{w.name} rank {rank}; exchanges simulated by device copies inside the timing"
+    return res
 
 
 def legs(w, q, dev, reps):
@@ -340,6 +365,8 @@ def main():
         if w.dtype == torch.bfloat16:
             log("[bench] leg: backward ring pass")
             rec["legs"]["backward"] = time_backward(w, args.rank, q, segs, kv, out, lse, reps=10)
+        log("[bench] leg: all-gather and all-to-all on heads")
+        rec["legs"]["variants"] = time_variants(w, args.rank, q, segs, kv, reps=5)
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_budget:.0f} s")
         rec["cpu_baseline"] = cpu_baseline(w, args.rank, segs, args.cpu_budget)
