@@ -38,9 +38,12 @@
 namespace ra {
 namespace {
 
-constexpr int kBW = 4;                // waves per workgroup
+constexpr int kBW = 4;                // waves per workgroup of the dQ kernel
 constexpr int kBThreads = 64 * kBW;
-constexpr int kOwn = 32 * kBW;        // owned rows per workgroup
+constexpr int kOwn = 32 * kBW;        // owned rows per workgroup of the dQ kernel
+constexpr int kKW = 8;                // waves per workgroup of the dK/dV kernel
+constexpr int kKThreads = 64 * kKW;
+constexpr int kKOwn = 32 * kKW;       // owned keys per workgroup of the dK/dV kernel
 constexpr int kT = 64;                // streamed rows per tile
 constexpr int kRunB = 1088;           // LDS bytes per 64-row run of one 16-byte column
 constexpr int kXcdsB = 8;
@@ -49,10 +52,9 @@ template <int D>
 struct BLay {
   static constexpr int NRUN = D / 8;               // 16-byte columns = load runs per tile
   static constexpr int TBYTES = NRUN * kRunB;      // one tensor's tile
-  static constexpr int RUNS_PER_WAVE = NRUN / kBW;
   static constexpr int ROWV = 2 * kT * 4;          // lse (log2 units) and delta of a tile's rows
   static constexpr int STAGE = 2 * TBYTES + ROWV;
-  static_assert(NRUN % kBW == 0, "runs must split evenly over the waves");
+  static_assert(NRUN % kBW == 0 && NRUN % kKW == 0, "runs must split evenly over the waves");
   static constexpr int at(int row, int col) { return col * kRunB + 16 * row; }
 };
 
@@ -78,15 +80,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const bf16* base, i
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, rows * d * 2, 0x00020000);
 }
 
-// rows row0.. of a [rows, D] slice into a tile of the layout above; wave w
-// fills runs (16-byte columns) w*RUNS_PER_WAVE.., lane i brings row i
-template <int D>
+// rows row0.. of a [rows, D] slice into a tile of the layout above; wave w of
+// W fills runs (16-byte columns) w*NRUN/W.., lane i brings row i
+template <int D, int W>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* dst, int32_t row0, int w,
                                           int lane) {
-  using L = BLay<D>;
+  constexpr int RUNS = BLay<D>::NRUN / W;
 #pragma unroll
-  for (int i = 0; i < L::RUNS_PER_WAVE; ++i) {
-    const int r = w * L::RUNS_PER_WAVE + i;
+  for (int i = 0; i < RUNS; ++i) {
+    const int r = w * RUNS + i;
     bload_lds16(rs, dst + r * kRunB, lane * D * 2 + 16 * r, row0 * D * 2);
   }
 }
@@ -231,8 +233,8 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
   auto fetch = [&](int32_t n) {
     char* st = smem + (n & 1) * L::STAGE;
     const int32_t r0 = tile_row0(tr, n);
-    load_tile<D>(krs, st, r0, w, lane);
-    load_tile<D>(vrs, st + L::TBYTES, r0, w, lane);
+    load_tile<D, kBW>(krs, st, r0, w, lane);
+    load_tile<D, kBW>(vrs, st + L::TBYTES, r0, w, lane);
   };
   fetch(0);
 
@@ -314,9 +316,12 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: owned keys, streamed Q/dO tiles
+// dK, dV: owned keys, streamed Q/dO tiles. Eight waves (256 owned keys): the
+// owned V rows sit in LDS (four 64-row tiles of the same layout) and are read
+// as B operands, which keeps a wave within 256 registers, so two waves share
+// each SIMD and one's exponentials overlap the other's products.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
     int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, float scale,
@@ -324,12 +329,13 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
     int32_t group) {
   using L = BLay<D>;
   constexpr int KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE + (kKOwn / kT) * L::TBYTES];
+  char* const vown = smem + 2 * L::STAGE;  // the owned V rows, 64 per tile
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int32_t logical = xcd_logical(per_xcd);
   if (logical >= nb * nkt) return;  // nb counts K/V slices here
   const int32_t prob = logical / nkt;  // K/V slice; its query slices are prob*group ..
-  const int32_t k0 = (logical - prob * nkt) * kOwn;
+  const int32_t k0 = (logical - prob * nkt) * kKOwn;
 
   const int32_t w_r0 = k0 + 32 * w;
   const int32_t krow = w_r0 + l32;
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
   TileRuns tr{0, 0, 0, 0};
   if (CAUSAL) {
     int32_t lo, hi;
-    seg_range(ks, k0, min(k0 + kOwn, Lk), lo, hi);
+    seg_range(ks, k0, min(k0 + kKOwn, Lk), lo, hi);
     tr = tiles_from(qs, Lq, lo, 0, true);
   } else {
     tr.n0 = tr.n = (Lq + kT - 1) / kT;
@@ -391,20 +397,23 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
     char* st = smem + (n & 1) * L::STAGE;
     const size_t rbase = qslice(n) * Lq;
     const int32_t r0 = qtile(n);
-    load_tile<D>(slice_rsrc(Q + rbase * D, Lq, D), st, r0, w, lane);
-    load_tile<D>(slice_rsrc(dO + rbase * D, Lq, D), st + L::TBYTES, r0, w, lane);
+    load_tile<D, kKW>(slice_rsrc(Q + rbase * D, Lq, D), st, r0, w, lane);
+    load_tile<D, kKW>(slice_rsrc(dO + rbase * D, Lq, D), st + L::TBYTES, r0, w, lane);
   };
   fetch_rowv(0);
   fetch(0);
-
-  bf16x8 kf[KS], vf[KS];
-  const bf16* kp = K + (kb + krow_c) * D + 8 * h;
-  const bf16* vp = V + (kb + krow_c) * D + 8 * h;
+  {
+    const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + kb * D, Lk, D);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    kf[s] = *(const bf16x8*)(kp + 16 * s);
-    vf[s] = *(const bf16x8*)(vp + 16 * s);
+    for (int j = 0; j < kKOwn / kT; ++j) load_tile<D, kKW>(vrs, vown + j * L::TBYTES, k0 + kT * j, w, lane);
   }
+  // this wave's 32 owned V rows: rows 32(w%2).. of owned tile w/2
+  const char* vw = vown + (w >> 1) * L::TBYTES;
+
+  bf16x8 kf[KS];
+  const bf16* kp = K + (kb + krow_c) * D + 8 * h;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kf[s] = *(const bf16x8*)(kp + 16 * s);
   f32x16 ak[DT], av[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) ak[t] = av[t] = f32x16{};
@@ -436,7 +445,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int ksi = 0; ksi < KS; ++ksi) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qt, st, ksi, l32, h), kf[ksi], s, 0, 0, 0);
-        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(dt, st, ksi, l32, h), vf[ksi], dpv, 0, 0, 0);
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(dt, st, ksi, l32, h),
+                                                      row_operand<D>(vw, w & 1, ksi, l32, h), dpv, 0, 0, 0);
       }
       f32x16 p, ds;
 #pragma unroll
@@ -515,7 +525,7 @@ DevSegs bdev(const HostSegs& s) { return DevSegs{s.start0, s.start1, s.len0, s.l
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
-  const int32_t nqt = (a.Lq + kOwn - 1) / kOwn, nkt = (a.Lk + kOwn - 1) / kOwn;
+  const int32_t nqt = (a.Lq + kOwn - 1) / kOwn, nkt = (a.Lk + kKOwn - 1) / kKOwn;
   const int32_t nkv = a.nb / a.group;
   const int32_t pq = (int32_t)(((int64_t)a.nb * nqt + kXcdsB - 1) / kXcdsB);
   const int32_t pk = (int32_t)(((int64_t)nkv * nkt + kXcdsB - 1) / kXcdsB);
@@ -525,7 +535,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
                      (int32_t)a.init_dq, a.dq, nqt, pq, a.group);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(kXcdsB * pk), dim3(kBThreads), 0, st,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(kXcdsB * pk), dim3(kKThreads), 0, st,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
                      a.lse, a.delta, nkv, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
                      (int32_t)a.init_dkv, a.dk, a.dv, nkt, pk, a.group);
