@@ -768,3 +768,34 @@ def test_head_all_to_all_every_group(gpu_lib, wname):
         mx, mr = compare(outs[r].float().cpu().double().numpy(), ro)
         print(f"rank {r} reassembled: max_abs={mx:.3e} mean_rel={mr:.3e}", flush=True)
         assert mx <= 2e-2 and mr <= 1e-2
+
+
+def test_variants_llm_32k_sampled(gpu_lib):
+    # the configuration the bench times: rank 0 / head group 0 of the 32K causal share
+    w = configs.LLM_32K_CP4
+    banner(f"all-gather and all-to-all on heads, {w.name}, sampled rows")
+    case = RingCase(w, 0)
+    out, lse = variants.run_allgather(case.q, case.q_segs, case.kv, case.kv_segs, True, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 0)
+    ro, rl = case.expected(rows)
+    idx = torch.as_tensor(rows, device=out.device)
+    assert_close(out.index_select(2, idx).float().cpu().double().numpy(), ro,
+                 lse.index_select(2, idx).cpu().double().numpy(), rl, w.dtype, "all-gather 32K r0")
+    del out, lse
+    segs = [case.kv_segs[t] for t in range(w.P)]
+    qb = [case.q] + [seeded.gen_bhsd_at(w.wid, seeded.Q, w.B, w.H, ringcase_positions(w, t), w.d, w.dtype, "cuda")
+                     for t in range(1, w.P)]
+    og, lg = variants.run_head_group(qb, case.kv, segs, 0, True, scale=w.scale)
+    torch.cuda.synchronize()
+    hg = w.H // w.P
+    pos = np.unique(np.concatenate([np.array([0, w.S - 1]), seeded.uniform_sample([77, w.wid], w.S, 128)]))
+    allpos = np.arange(w.S)
+    gpu_o = og.index_select(2, torch.as_tensor(pos, device=og.device)).float().cpu().double().numpy()
+    gpu_l = lg.index_select(2, torch.as_tensor(pos, device=lg.device)).cpu().double().numpy()
+    ref_o, ref_l = np.zeros_like(gpu_o), np.zeros_like(gpu_l)
+    for j in range(hg):
+        ex = lambda tid, r: seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, tid, 0, j, r, w.d), w.dtype))
+        ref_o[0, j], ref_l[0, j] = oracle.attention_rows(ex(seeded.Q, pos), pos, ex(seeded.K, allpos),
+                                                         ex(seeded.V, allpos), allpos, w.scale, True)
+    assert_close(gpu_o, ref_o, gpu_l, ref_l, w.dtype, f"head group 0 (heads 0..{hg - 1}), {pos.size} positions")
