@@ -47,7 +47,7 @@ extern "C" {
 typedef enum ra_status {
   RA_OK = 0,
   RA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent segments, aliasing */
-  RA_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (d, dtype) */
+  RA_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement (d, dtype) */
   RA_ERR_HIP = 3           /* a HIP call failed; see ra_last_hip_error() */
 } ra_status;
 

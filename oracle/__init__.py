@@ -1,6 +1,6 @@
 """CPU oracle for the ring-attention hot path (test infrastructure only).
 
-This package is the reference against which the HIP kernels are judged. It is
+This package is the reference against which the HIP kernels are checked. It is
 plain, slow and written to be checked by eye against the pages that describe
 the method. It shares no code with ``context_attention_ra_amd`` and imports
 nothing from it; only the seeded input generator (``seeded``) serves both.
