@@ -4,10 +4,11 @@
   all-gather next to ring-based exchange of K/V blocks. Every rank gathers all
   K/V blocks at their global positions, then attends its local queries to the
   whole sequence in one step.
-* All-to-all on heads: the k8ai page ("An alternative: all-to-all on heads")
-  switches from splitting by sequence to splitting by heads around the
-  attention and back; the degree is limited by the head count. Rank g holds
-  every position of heads [g*H/P, (g+1)*H/P) and runs plain attention on them.
+* All-to-all on heads: in the scheme of the k8ai page ("An alternative:
+  all-to-all on heads") the ranks trade their token ranges for head groups
+  before the attention and trade back after it, so the number of heads bounds
+  how many ranks can take part. Rank g holds every position of heads
+  [g*H/P, (g+1)*H/P) and runs plain attention on them.
 
 The exchanges are simulated by ``ra_copy_rows`` (strided device-to-device
 copies on the current stream); the attention itself is the library's step
