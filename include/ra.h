@@ -219,7 +219,8 @@ ra_status ra_bwd_prep(const void* out, const void* dout, ra_dtype dt, int32_t B,
  * accumulation). The two kernels run one after the other on `stream`.
  * Errors: those of ra_step_gqa, RA_ERR_INVALID_ARG for a null dout, lse, delta or
  *   accumulator, unknown flags, or an accumulator overlapping an input or
- *   another accumulator; RA_ERR_UNSUPPORTED for dt != RA_BF16.
+ *   another accumulator; RA_ERR_UNSUPPORTED for dt != RA_BF16 or more than
+ *   2^30 (K/V head, 256-key tile) pairs.
  */
 ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, const float* delta, ra_dtype dt,

@@ -192,6 +192,21 @@ def test_step_bwd_rejects_bad_arguments(lib, kw, expect):
     assert step_bwd(lib, **kw) == expect
 
 
+def test_step_bwd_refuses_grids_past_32_bits(lib):
+    # 2^15 heads of 2^24 keys at d=64 pass every other check (fake pointers 2^48 apart, so
+    # no span overlaps) but give 2^31 (K/V head, 256-key tile) pairs
+    H, Lk = 1 << 15, 1 << 24
+    a, b = _lib.segs([(0, 64)]), _lib.segs([(0, Lk)])
+    p = [(i + 1) << 48 for i in range(9)]
+    st = lib.ra_step_bwd(p[0], p[1], p[2], p[3], p[4], p[5], 1, 1, H, H, 64, Lk, 64, ctypes.byref(a),
+                         ctypes.byref(b), 1, 0.1, 3, p[6], p[7], p[8], None)
+    assert st == UNS
+    # one K/V head fewer per group of two: half the tiles, within the limit -> would launch,
+    # so only the head check is exercised here with an invalid grouping
+    assert lib.ra_step_bwd(p[0], p[1], p[2], p[3], p[4], p[5], 1, 1, H, 3, 64, Lk, 64, ctypes.byref(a),
+                           ctypes.byref(b), 1, 0.1, 3, p[6], p[7], p[8], None) == INV
+
+
 def test_bwd_prep_validation(lib):
     p = lib.ra_bwd_prep
     assert p(None, ptr(1), 1, 1, 1, 64, 128, ptr(2), None) == INV
