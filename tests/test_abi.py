@@ -201,8 +201,7 @@ def test_step_bwd_refuses_grids_past_32_bits(lib):
     st = lib.ra_step_bwd(p[0], p[1], p[2], p[3], p[4], p[5], 1, 1, H, H, 64, Lk, 64, ctypes.byref(a),
                          ctypes.byref(b), 1, 0.1, 3, p[6], p[7], p[8], None)
     assert st == UNS
-    # one K/V head fewer per group of two: half the tiles, within the limit -> would launch,
-    # so only the head check is exercised here with an invalid grouping
+    # an invalid grouping is refused first, as an argument error
     assert lib.ra_step_bwd(p[0], p[1], p[2], p[3], p[4], p[5], 1, 1, H, 3, 64, Lk, 64, ctypes.byref(a),
                            ctypes.byref(b), 1, 0.1, 3, p[6], p[7], p[8], None) == INV
 
