@@ -799,3 +799,68 @@ def test_variants_llm_32k_sampled(gpu_lib):
         ref_o[0, j], ref_l[0, j] = oracle.attention_rows(ex(seeded.Q, pos), pos, ex(seeded.K, allpos),
                                                          ex(seeded.V, allpos), allpos, w.scale, True)
     assert_close(gpu_o, ref_o, gpu_l, ref_l, w.dtype, f"head group 0 (heads 0..{hg - 1}), {pos.size} positions")
+
+
+# ---- seeded random segment tables: tile classification and masks -------------------
+
+def _random_runs(rng, n_rows, max_start):
+    """One or two runs of global positions that tile n_rows local rows."""
+    if n_rows >= 2 and rng.random() < 0.6:
+        n0 = int(rng.integers(1, n_rows))
+        s0 = int(rng.integers(0, max_start))
+        s1 = int(rng.integers(0, max_start))
+        return [(s0, n0), (s1, n_rows - n0)]
+    return [(int(rng.integers(0, max_start)), n_rows)]
+
+
+def _random_case(seed):
+    rng = np.random.default_rng([4242, seed])
+    d = int(rng.choice([64, 128]))
+    H_kv = int(rng.choice([1, 2]))
+    H = H_kv * int(rng.choice([1, 2, 3]))
+    B = int(rng.choice([1, 2]))
+    Lq = int(rng.integers(1, 700))
+    Lk = int(rng.integers(1, 700))
+    causal = bool(rng.random() < 0.7)
+    return B, H, H_kv, Lq, _random_runs(rng, Lq, 1500), Lk, _random_runs(rng, Lk, 1500), d, causal
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_segments_forward_and_backward(gpu_lib, seed):
+    B, H, Hkv, Lq, qr, Lk, kr, d, causal = _random_case(seed)
+    banner(f"random case {seed}: B{B} H{H} H_kv{Hkv} Lq{Lq} {qr} Lk{Lk} {kr} d{d} causal={causal}")
+    dt = torch.bfloat16
+    q = seeded.gen_bhsd(500 + seed, 0, B, H, 0, Lq, d, dt, "cuda")
+    k = seeded.gen_bhsd(500 + seed, 1, B, Hkv, 0, Lk, d, dt, "cuda")
+    v = seeded.gen_bhsd(500 + seed, 2, B, Hkv, 0, Lk, d, dt, "cuda")
+    do = seeded.gen_bhsd(500 + seed, DOUT, B, H, 0, Lq, d, dt, "cuda")
+    scale = d ** -0.5
+    st = ring.RingState(B, H, Lq, d, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    _lib.ra_step_final(q, k, v, qr, kr, causal, scale, st.o, st.m, st.l, out, lse, init=True)
+    delta = torch.empty_like(lse)
+    _lib.ra_bwd_prep(out, do, delta)
+    dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((B, Hkv, Lk, d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    _lib.ra_step_bwd(q, k, v, do, lse, delta, qr, kr, causal, scale, dq, dk, dv, init_dq=True, init_dkv=True)
+    torch.cuda.synchronize()
+    qp, kp = _runs_pos(qr), _runs_pos(kr)
+    qc, kc, vc, dc = (seeded.exact_f64(t.cpu()) for t in (q, k, v, do))
+    ro, rl = np.zeros((B, H, Lq, d)), np.zeros((B, H, Lq))
+    rq, rk, rv = np.zeros((B, H, Lq, d)), np.zeros((B, Hkv, Lk, d)), np.zeros((B, Hkv, Lk, d))
+    for b in range(B):
+        ro[b], rl[b] = oracle.grouped_attention(qc[b], qp, kc[b], vc[b], kp, scale, causal)
+        rq[b], rk[b], rv[b] = oracle.grouped_attention_grads(qc[b], qp, kc[b], vc[b], kp, scale, causal, dc[b])
+    go, gl = out.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    empty = ~np.isfinite(rl)
+    assert np.array_equal(empty, ~np.isfinite(gl)), "rows without visible keys must give lse = -inf"
+    assert np.all(go[empty] == 0.0)
+    assert_close(go, ro, np.where(empty, 0.0, gl), np.where(empty, 0.0, rl), dt, f"random {seed} forward")
+    for g, r, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        assert torch.isfinite(g).all(), n
+        if np.abs(r).max() == 0.0:  # nothing visible at all: the gradient is exactly zero
+            assert torch.all(g == 0), n
+        else:
+            grad_close(g.cpu().double().numpy(), r, f"random {seed} {n}")
