@@ -255,3 +255,17 @@ def test_variants_refuse_segments_that_do_not_tile_the_sequence():
     with pytest.raises(ValueError):
         variants._global_length([[(0, 10)], [(5, 10)]])
     assert variants._global_length([[(0, 4), (12, 4)], [(4, 8)]]) == 16
+
+
+def test_ring_drivers_refuse_bad_block_orders():
+    # the order is checked on the host before any buffer is made or any call is made
+    import torch
+    from context_attention_ra_amd import ring
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    kv = [(torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16),) * 2 for _ in range(3)]
+    segs = [[(64 * t, 64)] for t in range(3)]
+    for order in ([0, 1, 1], [0, 1], [2, 1, 0, 3]):
+        with pytest.raises(ValueError):
+            ring.run(q, segs[0], kv, segs, 0, True, order=order)
+        with pytest.raises(ValueError):
+            ring.run_bwd(q, segs[0], kv, segs, 0, True, q, torch.zeros((1, 1, 64)), q, order=order)
