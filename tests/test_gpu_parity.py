@@ -864,3 +864,33 @@ def test_random_segments_forward_and_backward(gpu_lib, seed):
             assert torch.all(g == 0), n
         else:
             grad_close(g.cpu().double().numpy(), r, f"random {seed} {n}")
+
+
+# ---- the ring as a differentiable PyTorch operation ----------------------------------
+
+def test_autograd_ring_attention_both_ranks(gpu_lib):
+    from context_attention_ra_amd.autograd import ring_attention
+    w = configs.CAUSAL_2RANK
+    banner(f"autograd ring attention, {w.name}, both ranks through one loss")
+    cases = [RingCase(w, r) for r in range(w.P)]
+    kv = [(k.clone().requires_grad_(True), v.clone().requires_grad_(True)) for k, v in cases[0].kv]
+    qs = [c.q.clone().requires_grad_(True) for c in cases]
+    dos = [seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, ringcase_positions(w, r), w.d, w.dtype, "cuda")
+           for r in range(w.P)]
+    loss = 0.0
+    for r, c in enumerate(cases):
+        out = ring_attention(qs[r], c.q_segs, kv, c.kv_segs, r, w.causal, scale=w.scale)
+        loss = loss + (out.float() * dos[r].float()).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    allpos = np.arange(w.S)
+    for h in range(w.H):
+        ex = lambda tid: seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, tid, 0, h, allpos, w.d),
+                                                          w.dtype))
+        rq, rk, rv = oracle.attention_grads(ex(seeded.Q), allpos, ex(seeded.K), ex(seeded.V), allpos, w.scale,
+                                            w.causal, ex(DOUT))
+        for r in range(w.P):
+            pos = ringcase_positions(w, r)
+            grad_close(qs[r].grad[0, h].float().cpu().double().numpy(), rq[pos], f"q.grad rank {r} h{h}")
+            grad_close(kv[r][0].grad[0, h].float().cpu().double().numpy(), rk[pos], f"k.grad block {r} h{h}")
+            grad_close(kv[r][1].grad[0, h].float().cpu().double().numpy(), rv[pos], f"v.grad block {r} h{h}")
