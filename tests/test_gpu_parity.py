@@ -894,3 +894,26 @@ def test_autograd_ring_attention_both_ranks(gpu_lib):
             grad_close(qs[r].grad[0, h].float().cpu().double().numpy(), rq[pos], f"q.grad rank {r} h{h}")
             grad_close(kv[r][0].grad[0, h].float().cpu().double().numpy(), rk[pos], f"k.grad block {r} h{h}")
             grad_close(kv[r][1].grad[0, h].float().cpu().double().numpy(), rv[pos], f"v.grad block {r} h{h}")
+
+
+@pytest.mark.parametrize("split,P,causal,dtype", [("zigzag", 2, True, torch.bfloat16),
+                                                  ("zigzag", 4, True, torch.bfloat16),
+                                                  ("contiguous", 3, False, torch.bfloat16),
+                                                  ("contiguous", 4, True, torch.float32),
+                                                  ("temporal", 4, False, torch.bfloat16)])
+def test_context_parallel_attention_whole_sequence(gpu_lib, split, P, causal, dtype):
+    from context_attention_ra_amd.cp import context_parallel_attention
+    B, H, H_kv, d = 1, 4, 2, 64
+    S_sp = 96 if split == "temporal" else 0
+    S = 8 * 96 if split == "temporal" else (768 if P == 3 else 1024)
+    banner(f"context-parallel attention of a whole sequence: {split} P={P} causal={causal} {dtype} S={S}")
+    q = seeded.gen_bhsd(600, 0, B, H, 0, S, d, dtype, "cuda")
+    k = seeded.gen_bhsd(600, 1, B, H_kv, 0, S, d, dtype, "cuda")
+    v = seeded.gen_bhsd(600, 2, B, H_kv, 0, S, d, dtype, "cuda")
+    out, lse = context_parallel_attention(q, k, v, P, split=split, causal=causal, S_sp=S_sp)
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    qc, kc, vc = (seeded.exact_f64(t.cpu()) for t in (q, k, v))
+    ro, rl = oracle.grouped_attention(qc[0], pos, kc[0], vc[0], pos, d ** -0.5, causal)
+    assert_close(out[0].float().cpu().double().numpy(), ro, lse[0].cpu().double().numpy(), rl, dtype,
+                 f"whole sequence {split} P={P}")
