@@ -69,3 +69,51 @@ def context_parallel_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         outs.append(out)
         lses.append(lse.unsqueeze(-1))
     return unshard(outs, segs, S), unshard(lses, segs, S)[..., 0]
+
+
+class _Shard(torch.autograd.Function):
+    """``shard`` with the reassembly of the shares' gradients as its backward."""
+
+    @staticmethod
+    def forward(ctx, x, segs):
+        ctx.segs, ctx.S = segs, x.shape[-2]
+        return tuple(shard(x, segs))
+
+    @staticmethod
+    def backward(ctx, *grads):
+        parts = [g.contiguous() for g in grads]
+        return unshard(parts, ctx.segs, ctx.S), None
+
+
+class _Unshard(torch.autograd.Function):
+    """``unshard`` with the split of the output gradient as its backward."""
+
+    @staticmethod
+    def forward(ctx, segs, S, *parts):
+        ctx.segs = segs
+        return unshard(parts, segs, S)
+
+    @staticmethod
+    def backward(ctx, g):
+        return (None, None, *shard(g.contiguous(), ctx.segs))
+
+
+def cp_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: int, split: str = "zigzag",
+                 causal: bool = True, scale: Optional[float] = None, S_sp: int = 0) -> torch.Tensor:
+    """``context_parallel_attention`` as a differentiable operation (bf16).
+
+    Returns the output [B, H, S, d] in global order; ``backward`` runs every
+    rank's backward ring and returns whole-sequence gradients of q, k and v
+    (the K/V block gradients of all ranks added, as the travelling dK/dV of a
+    real ring are).
+    """
+    from .autograd import ring_attention
+
+    S = q.shape[2]
+    segs = [layout.split(split, S, P, r, S_sp=S_sp) for r in range(P)]
+    qs = _Shard.apply(q, segs)
+    ks = _Shard.apply(k, segs)
+    vs = _Shard.apply(v, segs)
+    kv = list(zip(ks, vs))
+    outs = [ring_attention(qs[r], segs[r], kv, segs, r, causal, scale=scale) for r in range(P)]
+    return _Unshard.apply(segs, S, *outs)

@@ -917,3 +917,24 @@ def test_context_parallel_attention_whole_sequence(gpu_lib, split, P, causal, dt
     ro, rl = oracle.grouped_attention(qc[0], pos, kc[0], vc[0], pos, d ** -0.5, causal)
     assert_close(out[0].float().cpu().double().numpy(), ro, lse[0].cpu().double().numpy(), rl, dtype,
                  f"whole sequence {split} P={P}")
+
+
+def test_cp_attention_gradients_whole_sequence(gpu_lib):
+    from context_attention_ra_amd.cp import cp_attention
+    B, H, H_kv, d, S, P = 1, 4, 2, 64, 1024, 2
+    banner(f"differentiable whole-sequence attention: zigzag P={P}, H={H}, H_kv={H_kv}, S={S}")
+    dt = torch.bfloat16
+    q, k, v = (seeded.gen_bhsd(610, t, B, hh, 0, S, d, dt, "cuda").requires_grad_(True)
+               for t, hh in ((0, H), (1, H_kv), (2, H_kv)))
+    do = seeded.gen_bhsd(610, DOUT, B, H, 0, S, d, dt, "cuda")
+    out = cp_attention(q, k, v, P, split="zigzag", causal=True)
+    (out.float() * do.float()).sum().backward()
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    qc, kc, vc, dc = (seeded.exact_f64(t.detach().cpu()) for t in (q, k, v, do))
+    ro, _ = oracle.grouped_attention(qc[0], pos, kc[0], vc[0], pos, d ** -0.5, True)
+    rq, rk, rv = oracle.grouped_attention_grads(qc[0], pos, kc[0], vc[0], pos, d ** -0.5, True, dc[0])
+    mx, mr = compare(out[0].detach().float().cpu().double().numpy(), ro)
+    assert mx <= 2e-2 and mr <= 1e-2, (mx, mr)
+    for t, r, n in ((q, rq, "q"), (k, rk, "k"), (v, rv, "v")):
+        grad_close(t.grad[0].float().cpu().double().numpy(), r, f"whole-sequence {n}.grad")
