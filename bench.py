@@ -272,7 +272,13 @@ def cpu_baseline(w, rank, segs, budget_s):
         heads.add(h)
         i += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    rows_per_s = done_rows / elapsed
+    full_rows = w.B * w.H * qpos_all.size
     return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "rows_per_s": rows_per_s,
+            "extrapolated_full_s": full_rows / rows_per_s,
+            "extrapolation": f"{full_rows} query rows of the rank's share (B*H*local rows) at the sampled "
+                             f"rows/s; extrapolated, not measured",
             "sample": f"{done_rows} query rows ({i} runs of {chunk} rows from {len(heads)} heads) of rank {rank} "
                       f"against the full {w.S}-token K/V, fp64 numpy; {elapsed:.1f} s",
             "host_cpus": len(os.sched_getaffinity(0))}
