@@ -13,3 +13,18 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_cpu_baseline_leg_reports_its_sample():
+    # the oracle leg runs on the host: a short budget on the tiny fp32 workload
+    sys.path.insert(0, ROOT)
+    import bench
+    from context_attention_ra_amd import configs, layout
+    w = configs.TINY_F32
+    segs = [layout.split(w.split, w.S, w.P, t) for t in range(w.P)]
+    rec = bench.cpu_baseline(w, 0, segs, 0.5)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s" and rec["value"] > 0
+    assert rec["cores"] >= 1 and rec["rows_per_s"] > 0
+    full_rows = w.B * w.H * w.L
+    assert abs(rec["extrapolated_full_s"] - full_rows / rec["rows_per_s"]) < 1e-9 * rec["extrapolated_full_s"] + 1e-12
+    assert "extrapolated" in rec["extrapolation"] and "query rows" in rec["sample"]
