@@ -142,6 +142,20 @@ def time_kernel(fn, reps, warmup=3):
     return float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)]))
 
 
+def plain_gemm(dev, n=8192, reps=20):
+    """A plain bf16 GEMM through PyTorch (hipBLASLt), n x n x n, timed with HIP
+    events: what the matrix cores sustain for a large dense product on this
+    chip, the counterpart of the plain stream beside the HBM-bound legs."""
+    g = torch.Generator(device=dev).manual_seed(20262)
+    a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    ms = time_kernel(lambda: torch.matmul(a, b, out=c), reps, warmup=20)
+    fl = 2.0 * n ** 3
+    return {"TFLOP/s": fl / ms / 1e9, "frac_of_peak": fl / ms / 1e-3 / PEAK_BF16_DENSE,
+            "shape": f"bf16 [{n},{n}] x [{n},{n}] -> bf16, fp32 accumulate (torch.matmul)", "ms": ms}
+
+
 def time_backward(w, rank, q, segs, kv, out, lse, reps, warmup=3):
     """The backward pass of the same share: ra_bwd_prep and P ra_step_bwd
     launches (dQ kernel, then dK/dV kernel), timed with HIP events on the
@@ -350,6 +364,7 @@ def main():
     k_mean_ms = float(kms.mean())
     achieved = (total / w.P) / (k_mean_ms * 1e-3)
     src_hash = kernel_source_hash(STEP_SOURCES[w.dtype])
+    gemm = plain_gemm(dev)
     traffic = load_traffic("ra_step:" + w.name, src_hash)
     rec = {
         "metric": "attention TFLOP/s per MI355X (and % bf16 MFMA peak), ring-step kernel",
@@ -375,7 +390,8 @@ def main():
                      "kernel_timing": f"HIP events around each ra_step launch on its stream, in every "
                                       f"{EVENT_EVERY}th timed pass ({kms.shape[0]} of {args.steps})",
                      "kernel_ms_per_ring_step": [float(x) for x in kms.mean(axis=0)],
-                     "flop_per_launch_mean": total / w.P},
+                     "flop_per_launch_mean": total / w.P,
+                     "plain_gemm": gemm, "vs_plain_gemm": achieved / 1e12 / gemm["TFLOP/s"]},
         "ring_ms_per_pass": ms_per_step,
         "kernel_share_of_pass": float(kms.sum(axis=1).mean()) / ms_per_step,
     }

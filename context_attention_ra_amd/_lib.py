@@ -20,6 +20,8 @@ RA_F32, RA_BF16 = 0, 1
 RA_MASK_NONE, RA_MASK_CAUSAL = 0, 1
 RA_STEP_INIT = 1
 RA_BWD_KV_INIT = 2
+RA_BWD_NO_DQ = 4
+RA_BWD_NO_DKV = 8
 
 # every symbol include/ra.h declares
 EXPORTS = ("ra_step", "ra_finalize", "ra_step_final", "ra_step_gqa", "ra_step_final_gqa",
@@ -199,7 +201,10 @@ def ra_bwd_prep(out, dout, delta, stream=None):
 
 
 def ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs, causal, scale, dq, dk, dv,
-                init_dq=False, init_dkv=False, stream=None):
+                init_dq=False, init_dkv=False, stream=None, parts="both"):
+    """parts: "both", "dq" (only the dQ kernel) or "dkv" (only the dK/dV kernel)."""
+    if parts not in ("both", "dq", "dkv"):
+        raise ValueError(f"parts must be 'both', 'dq' or 'dkv', not {parts!r}")
     _check_step(q, k, v, dq, lse, delta)
     _shape("dout", dout, q.shape)
     _shape("dk", dk, k.shape)
@@ -208,6 +213,7 @@ def ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs, causal, scale, dq, d
     H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
     flags = (RA_STEP_INIT if init_dq else 0) | (RA_BWD_KV_INIT if init_dkv else 0)
+    flags |= {"both": 0, "dq": RA_BWD_NO_DKV, "dkv": RA_BWD_NO_DQ}[parts]
     _check("ra_step_bwd", load().ra_step_bwd(
         _p(q), _p(k), _p(v), _p(dout), _p(lse), _p(delta), _dtype(q), B, H, H_kv, Lq, Lk, d,
         ctypes.byref(qs), ctypes.byref(ks), RA_MASK_CAUSAL if causal else RA_MASK_NONE,

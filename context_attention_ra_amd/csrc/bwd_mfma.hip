@@ -399,17 +399,22 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const int32_t nkv = a.nb / a.group;
   const int32_t pq = (int32_t)(((int64_t)a.nb * nqt + kXcdsB - 1) / kXcdsB);
   const int32_t pk = (int32_t)(((int64_t)nkv * nkt + kXcdsB - 1) / kXcdsB);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(kXcdsB * pq), dim3(kBThreads), 0, st,
-                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
-                     a.lse, a.delta, a.nb, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
-                     (int32_t)a.init_dq, a.dq, nqt, pq, a.group);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(kXcdsB * pk), dim3(kKThreads), 0, st,
-                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
-                     a.lse, a.delta, nkv, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
-                     (int32_t)a.init_dkv, a.dk, a.dv, nkt, pk, a.group);
-  return hipGetLastError();
+  if (a.run_dq) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(kXcdsB * pq), dim3(kBThreads), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
+                       a.lse, a.delta, a.nb, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
+                       (int32_t)a.init_dq, a.dq, nqt, pq, a.group);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.run_dkv) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(kXcdsB * pk), dim3(kKThreads), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
+                       a.lse, a.delta, nkv, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
+                       (int32_t)a.init_dkv, a.dk, a.dv, nkt, pk, a.group);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace

@@ -185,7 +185,8 @@ ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* d
                       const ra_segs* kv_segs, ra_mask mask, float scale, uint32_t flags,
                       float* dq_acc, float* dk_acc, float* dv_acc, hipStream_t stream) {
   if (!dout || !lse || !delta || !dq_acc || !dk_acc || !dv_acc) return RA_ERR_INVALID_ARG;
-  if (flags & ~(RA_STEP_INIT | RA_BWD_KV_INIT)) return RA_ERR_INVALID_ARG;
+  if (flags & ~(RA_STEP_INIT | RA_BWD_KV_INIT | RA_BWD_NO_DQ | RA_BWD_NO_DKV)) return RA_ERR_INVALID_ARG;
+  if ((flags & RA_BWD_NO_DQ) && (flags & RA_BWD_NO_DKV)) return RA_ERR_INVALID_ARG;
   // the forward checks cover q, k, v, the sizes, segments, mask and scale; dq_acc
   // and the two per-row vectors take the places of o_acc, m and l
   ra::StepArgs sa;
@@ -224,6 +225,8 @@ ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* d
   a.causal = sa.causal;
   a.init_dq = (flags & RA_STEP_INIT) != 0;
   a.init_dkv = (flags & RA_BWD_KV_INIT) != 0;
+  a.run_dq = (flags & RA_BWD_NO_DQ) == 0;
+  a.run_dkv = (flags & RA_BWD_NO_DKV) == 0;
   a.scale = scale;
   a.dq = dq_acc;
   a.dk = dk_acc;

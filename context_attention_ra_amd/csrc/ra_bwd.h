@@ -25,6 +25,8 @@ struct BwdArgs {
   bool causal;
   bool init_dq;   // dq starts at zero (not read)
   bool init_dkv;  // dk, dv start at zero (not read)
+  bool run_dq;    // launch the dQ kernel
+  bool run_dkv;   // launch the dK/dV kernel
   float scale;
   float* dq;
   float* dk;

@@ -179,6 +179,15 @@ ra_status ra_step_final_gqa(const void* q, const void* k, const void* v, ra_dtyp
  * dq_acc.) */
 #define RA_BWD_KV_INIT 2u
 
+/* ra_step_bwd flags that run half of a step: RA_BWD_NO_DQ launches only the
+ * dK/dV kernel (dq_acc is neither read nor written), RA_BWD_NO_DKV only the
+ * dQ kernel (dk_acc, dv_acc are neither read nor written). The two halves
+ * read the same inputs and write disjoint accumulators, so a caller may issue
+ * them on two streams; the accumulators of a skipped half are still checked
+ * as arguments. Setting both is an invalid argument. */
+#define RA_BWD_NO_DQ 4u
+#define RA_BWD_NO_DKV 8u
+
 /*
  * ra_bwd_prep — per-row delta_i = <dO_i, O_i> (fp32) of the final forward
  * output O and its upstream gradient dO, needed by every backward ring step.
@@ -213,12 +222,14 @@ ra_status ra_bwd_prep(const void* out, const void* dout, ra_dtype dt, int32_t B,
  * q_segs, kv_segs, mask, scale: as for ra_step (the same mask and scale as
  *          the forward pass)
  * flags    0, RA_STEP_INIT (dq_acc starts at zero), RA_BWD_KV_INIT (dk_acc,
- *          dv_acc start at zero), or both
+ *          dv_acc start at zero), or both; with at most one of RA_BWD_NO_DQ,
+ *          RA_BWD_NO_DKV to run half of the step
  * dq_acc   [B,H,Lq,d] fp32 in/out; dk_acc, dv_acc [B,H_kv,Lk,d] fp32 in/out
  * dt must be RA_BF16 (inputs bf16, products on the matrix cores, fp32
  * accumulation). The two kernels run one after the other on `stream`.
  * Errors: those of ra_step_gqa, RA_ERR_INVALID_ARG for a null dout, lse, delta or
- *   accumulator, unknown flags, or an accumulator overlapping an input or
+ *   accumulator, unknown flags, both RA_BWD_NO_DQ and RA_BWD_NO_DKV, or an
+ *   accumulator overlapping an input or
  *   another accumulator; RA_ERR_UNSUPPORTED for dt != RA_BF16 or more than
  *   2^30 (K/V head, 256-key tile) pairs.
  */

@@ -180,7 +180,10 @@ def step_bwd(lib, dt=1, d=128, flags=3, q=None, dout=None, lse=None, delta=None,
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(dout=0), INV), (dict(lse=0), INV), (dict(delta=0), INV), (dict(dq=0), INV),
-    (dict(dk=0), INV), (dict(dv=0), INV), (dict(flags=4), INV),
+    (dict(dk=0), INV), (dict(dv=0), INV), (dict(flags=16), INV),
+    (dict(flags=4 | 8), INV),          # both halves skipped
+    (dict(flags=4 | 3, d=96), UNS), (dict(flags=8 | 3, d=96), UNS),  # one half: valid flags
+    (dict(flags=4, dq=0), INV),        # a skipped half's accumulator is still checked
     (dict(dk=ptr(1)), INV),            # dk accumulator over the keys
     (dict(dv=ptr(7) + 256), INV),      # dv overlapping dk
     (dict(dq=ptr(3)), INV),            # dq over the upstream gradient
@@ -231,6 +234,9 @@ def test_binding_checks_shapes_before_calling():
     with pytest.raises(ValueError):  # dk/dv accumulators shaped like the K/V block
         _lib.ra_step_bwd(q, k2, k2, q, st[1], st[2], [(0, 64)], [(0, 64)], True, 0.1, st[0],
                          torch.zeros((1, 4, 64, 64)), torch.zeros((1, 4, 64, 64)))
+    with pytest.raises(ValueError):  # a half of the step that does not exist
+        _lib.ra_step_bwd(q, k2, k2, q, st[1], st[2], [(0, 64)], [(0, 64)], True, 0.1, st[0],
+                         torch.zeros((1, 2, 64, 64)), torch.zeros((1, 2, 64, 64)), parts="dk")
     with pytest.raises(ValueError):
         _lib.ra_finalize(st[0], st[1], st[2], torch.zeros((1, 4, 63, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError):

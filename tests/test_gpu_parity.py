@@ -591,6 +591,25 @@ def test_bwd_accumulates(gpu_lib):
         assert torch.allclose(a, 2 * o, rtol=1e-6, atol=1e-6)
 
 
+def test_bwd_halves_touch_only_their_accumulators(gpu_lib):
+    banner("ra_step_bwd halves: parts='dq' and parts='dkv' against the whole step")
+    B, H, L, d = 1, 2, 200, 128
+    dt = torch.bfloat16
+    q, k, v, do = (seeded.gen_bhsd(321, t, B, H, 0, L, d, dt, "cuda") for t in range(4))
+    lse = torch.full((B, H, L), 5.0, device="cuda")
+    delta = torch.full((B, H, L), 0.25, device="cuda")
+    new = lambda: [torch.full((B, H, L, d), float("nan"), device="cuda") for _ in range(3)]
+    both, dq_only, dkv_only = new(), new(), new()
+    args = (q, k, v, do, lse, delta, [(0, L)], [(0, L)], True, 0.125)
+    _lib.ra_step_bwd(*args, *both, init_dq=True, init_dkv=True)
+    _lib.ra_step_bwd(*args, *dq_only, init_dq=True, init_dkv=True, parts="dq")
+    _lib.ra_step_bwd(*args, *dkv_only, init_dq=True, init_dkv=True, parts="dkv")
+    torch.cuda.synchronize()
+    assert torch.equal(dq_only[0], both[0]) and torch.isnan(dq_only[1]).all() and torch.isnan(dq_only[2]).all()
+    assert torch.isnan(dkv_only[0]).all()
+    assert torch.equal(dkv_only[1], both[1]) and torch.equal(dkv_only[2], both[2])
+
+
 def _bwd_ring_case(w):
     """Forward and backward of every rank of ring workload w; dK/dV accumulators
     travel over the ranks. Returns the GPU gradients and the per-rank cases."""
