@@ -691,6 +691,28 @@ def test_bwd_llm_32k_rank0_sampled_dq(gpu_lib):
         assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
 
 
+def test_bwd_llm_32k_rank0_dkdv_two_heads(gpu_lib):
+    # dK/dV of every block at the full share: rank 0's contributions, all key
+    # rows of heads 0 and H-1 (the oracle's full gradient costs about 10 s per head)
+    w = configs.LLM_32K_CP4
+    banner(f"backward ring, {w.name} rank 0: dk, dv of every block, heads 0 and {w.H - 1}")
+    case = RingCase(w, 0)
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, scale=w.scale)
+    qpos = ringcase_positions(w, 0)
+    do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, qpos, w.d, w.dtype, "cuda")
+    _, dkv = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, out, lse, do, scale=w.scale)
+    torch.cuda.synchronize()
+    allpos = np.arange(w.S)
+    for h in (0, w.H - 1):
+        ex = lambda tid, r: seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, tid, 0, h, r, w.d), w.dtype))
+        _, rk, rv = oracle.attention_grads(ex(seeded.Q, qpos), qpos, ex(seeded.K, allpos), ex(seeded.V, allpos),
+                                           allpos, w.scale, True, ex(DOUT, qpos))
+        for t in range(w.P):
+            kpos = ringcase_positions(w, t)
+            grad_close(dkv[t][0][0, h].cpu().double().numpy(), rk[kpos], f"dk block {t} h{h}")
+            grad_close(dkv[t][1][0, h].cpu().double().numpy(), rv[kpos], f"dv block {t} h{h}")
+
+
 @pytest.mark.parametrize("ci", [0, 1, 2])  # the bf16 cases (the backward step is bf16 only)
 def test_bwd_gqa_single_block(gpu_lib, ci):
     B, H, Hkv, Lq, qr, Lk, kr, d, causal, dt = GQA_CASES[ci]
