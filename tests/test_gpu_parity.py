@@ -760,6 +760,34 @@ def test_bwd_gqa_ring_causal_2rank_all_ranks(gpu_lib):
             grad_close(dkv[r][1][b].cpu().double().numpy(), rv[:, pos], f"dv block {r}")
 
 
+def test_bwd_gqa_llm_32k_rank0_last_kv_head(gpu_lib):
+    # grouped backward at the full 32K share (32 query heads over 8 K/V heads):
+    # dq of query heads 28..31 and dk, dv of K/V head 7, which they share, for
+    # every block; rank 0's contributions, exact from the oracle's gradients
+    w = configs.LLM_32K_CP4_GQA
+    G = w.H // w.Hkv
+    g = w.Hkv - 1
+    heads = list(range(g * G, (g + 1) * G))
+    banner(f"backward ring, {w.name} rank 0: query heads {heads[0]}..{heads[-1]} and their K/V head {g}")
+    case = RingCase(w, 0)
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, scale=w.scale)
+    qpos = ringcase_positions(w, 0)
+    do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, qpos, w.d, w.dtype, "cuda")
+    dq, dkv = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, out, lse, do, scale=w.scale)
+    torch.cuda.synchronize()
+    allpos = np.arange(w.S)
+    ex = lambda tid, h, r: seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, tid, 0, h, r, w.d), w.dtype))
+    gq = np.stack([ex(seeded.Q, h, qpos) for h in heads])
+    gdo = np.stack([ex(DOUT, h, qpos) for h in heads])
+    gk, gv = ex(seeded.K, g, allpos)[None], ex(seeded.V, g, allpos)[None]
+    rq, rk, rv = oracle.grouped_attention_grads(gq, qpos, gk, gv, allpos, w.scale, True, gdo)
+    grad_close(dq[0, heads[0]:heads[-1] + 1].cpu().double().numpy(), rq, f"dq heads {heads[0]}..{heads[-1]}")
+    for t in range(w.P):
+        kpos = ringcase_positions(w, t)
+        grad_close(dkv[t][0][0, g].cpu().double().numpy(), rk[0, kpos], f"dk block {t} kv head {g}")
+        grad_close(dkv[t][1][0, g].cpu().double().numpy(), rv[0, kpos], f"dv block {t} kv head {g}")
+
+
 # ---- the alternatives to the ring: all-gather and all-to-all on heads ------------------
 
 from context_attention_ra_amd import variants  # noqa: E402
