@@ -691,6 +691,33 @@ def test_bwd_llm_32k_rank0_sampled_dq(gpu_lib):
         assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
 
 
+@pytest.mark.slow
+def test_bwd_video_dit_432k_sampled_dq(gpu_lib):
+    # the backward ring at the video share (54,000 local queries against eight
+    # non-causal 54,000-token blocks: ragged 256-key tiles), dq of the sampled
+    # rows of three heads against the oracle; dk, dv must be finite
+    w = configs.VIDEO_DIT_CP8
+    rank = 3
+    banner(f"backward ring, {w.name} rank {rank}: dq on sampled rows of heads 0, 15, 31")
+    case = RingCase(w, rank)
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, rank, w.causal, scale=w.scale)
+    qpos = ringcase_positions(w, rank)
+    do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, qpos, w.d, w.dtype, "cuda")
+    dq, dkv = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, rank, w.causal, out, lse, do,
+                           scale=w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, rank)
+    allpos = np.arange(w.S)
+    for h in (0, 15, 31):
+        ex = lambda tid, r: seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, tid, 0, h, r, w.d), w.dtype))
+        ref, _, _ = oracle.attention_grads(ex(seeded.Q, qpos[rows]), qpos[rows], ex(seeded.K, allpos),
+                                           ex(seeded.V, allpos), allpos, w.scale, False, ex(DOUT, qpos[rows]))
+        gpu = dq[0, h].index_select(0, torch.as_tensor(rows, device=dq.device)).cpu().double().numpy()
+        grad_close(gpu, ref, f"{w.name} dq head {h}, {rows.size} rows")
+    for dk, dv in dkv:
+        assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
 def test_bwd_llm_32k_rank0_dkdv_two_heads(gpu_lib):
     # dK/dV of every block at the full share: rank 0's contributions, all key
     # rows of heads 0 and H-1 (the oracle's full gradient costs about 10 s per head)
