@@ -65,7 +65,11 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
   const int32_t logical = xcd_logical(per_xcd);
   if (logical >= nb * nqt) return;
   const int32_t prob = logical / nqt;
-  const int32_t q0 = (logical - prob * nqt) * kOwn;
+  // causal: the last query tiles of a slice see the most keys, so they are
+  // dispatched first and the light ones fill the tail (the workgroups of an
+  // XCD start in logical order as CUs free up)
+  const int32_t qt = logical - prob * nqt;
+  const int32_t q0 = (CAUSAL ? nqt - 1 - qt : qt) * kOwn;
 
   const int32_t w_r0 = q0 + 32 * w;
   const int32_t qrow = w_r0 + l32;
