@@ -147,7 +147,8 @@ def run_bwd(q: torch.Tensor,
             dout: torch.Tensor,
             scale: Optional[float] = None,
             order: Optional[List[int]] = None,
-            dkv: Optional[List[Tuple[torch.Tensor, torch.Tensor]]] = None):
+            dkv: Optional[List[Tuple[torch.Tensor, torch.Tensor]]] = None,
+            overlap: Optional[bool] = None):
     """Backward pass of rank `rank`'s share: P backward block steps.
 
     The ring passes the K/V blocks again in the backward pass (k8ai
@@ -160,6 +161,12 @@ def run_bwd(q: torch.Tensor,
     dkv        optional per-block (dk, dv) fp32 accumulators [B, H, Lk, d] that
                already hold other ranks' contributions (they are added to);
                None: fresh accumulators holding this rank's contributions only
+    overlap    run the dK/dV half of every step on a second stream, beside the
+               chain of dQ halves on the current stream (each block's dK/dV
+               depends on no other step), and make the current stream wait for
+               it before returning. None: only with grouped K/V heads, where
+               the dK/dV kernel is a single round of workgroups and the
+               causal imbalance of the diagonal step would leave CUs idle
     returns (dq [B, H, Lq, d] fp32, dkv)
     """
     P = len(kv_blocks)
@@ -179,10 +186,31 @@ def run_bwd(q: torch.Tensor,
     delta = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
     _lib.ra_bwd_prep(out, dout, delta, stream=stream)
     dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device=dev)
+    if overlap is None:
+        overlap = kv_blocks[0][0].shape[1] != H
+    side = None
+    if overlap:
+        side = torch.cuda.Stream(dev)
+        ready = torch.cuda.Event()
+        ready.record(stream)  # delta and every input are in place
+        side.wait_event(ready)
+        for x in (q, dout, lse, delta):
+            x.record_stream(side)
+        for (k, v), (dk, dv) in zip(kv_blocks, dkv):
+            for x in (k, v, dk, dv):
+                x.record_stream(side)
     for s in range(P):
         t = order[s]
         k, v = kv_blocks[t]
         dk, dv = dkv[t]
-        _lib.ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs[t], causal, scale, dq, dk, dv,
-                         init_dq=(s == 0), init_dkv=fresh, stream=stream)
+        args = (q, k, v, dout, lse, delta, q_segs, kv_segs[t], causal, scale, dq, dk, dv)
+        if side is None:
+            _lib.ra_step_bwd(*args, init_dq=(s == 0), init_dkv=fresh, stream=stream)
+        else:
+            _lib.ra_step_bwd(*args, init_dq=(s == 0), init_dkv=fresh, stream=side, parts="dkv")
+            _lib.ra_step_bwd(*args, init_dq=(s == 0), init_dkv=fresh, stream=stream, parts="dq")
+    if side is not None:
+        done = torch.cuda.Event()
+        done.record(side)
+        stream.wait_event(done)
     return dq, dkv

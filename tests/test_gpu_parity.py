@@ -610,6 +610,25 @@ def test_bwd_halves_touch_only_their_accumulators(gpu_lib):
     assert torch.equal(dkv_only[1], both[1]) and torch.equal(dkv_only[2], both[2])
 
 
+@pytest.mark.parametrize("wname", ["causal-bf16-4k-cp2", "causal-bf16-4k-cp2-gqa4", "llm-32k-causal-cp4-gqa4"])
+def test_bwd_ring_overlap_matches_one_stream(gpu_lib, wname):
+    # the dK/dV halves on a second stream are the same launches on the same
+    # inputs: every gradient is bitwise the one of the single-stream ring
+    w = configs.RING_WORKLOADS[wname]
+    rank = 0
+    banner(f"backward ring, {w.name} rank {rank}: dK/dV halves on a second stream vs one stream")
+    case = RingCase(w, rank)
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, rank, w.causal, scale=w.scale)
+    do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, ringcase_positions(w, rank), w.d, w.dtype, "cuda")
+    res = [ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, rank, w.causal, out, lse, do,
+                        scale=w.scale, overlap=ov) for ov in (False, True)]
+    torch.cuda.synchronize()
+    (dq1, kv1), (dq2, kv2) = res
+    assert torch.equal(dq1, dq2)
+    for (a, b), (c, e) in zip(kv1, kv2):
+        assert torch.equal(a, c) and torch.equal(b, e)
+
+
 def _bwd_ring_case(w):
     """Forward and backward of every rank of ring workload w; dK/dV accumulators
     travel over the ranks. Returns the GPU gradients and the per-rank cases."""
