@@ -206,6 +206,9 @@ ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* d
       if (overlap(acc[i], acc[j])) return RA_ERR_INVALID_ARG;
   }
   if (dt != RA_BF16) return RA_ERR_UNSUPPORTED;
+  // the dK/dV kernel streams the query and dO slices through buffer resources
+  // whose byte size is a 32-bit value, as the step kernels do for K/V
+  if ((int64_t)Lq * d * (int64_t)es > (int64_t)INT32_MAX) return RA_ERR_UNSUPPORTED;
   // the dK/dV kernel numbers its workgroups (K/V slice, 256-key tile) in 32 bits
   if ((int64_t)B * H_kv * ((Lk + 255) / 256) > (int64_t)INT32_MAX / 2) return RA_ERR_UNSUPPORTED;
   ra::BwdArgs a{};

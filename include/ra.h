@@ -103,7 +103,9 @@ typedef struct ra_segs {
  * dt: RA_BF16 (matrix-core path) or RA_F32 (fp32 vector path).
  * Errors: RA_ERR_INVALID_ARG for null pointers, B/H/Lq/Lk <= 0, bad segments,
  *   a non-finite or non-positive scale, unknown flags or mask, or o_acc/m/l
- *   overlapping q/k/v; RA_ERR_UNSUPPORTED for d not in {64, 128}.
+ *   overlapping q/k/v; RA_ERR_UNSUPPORTED for d not in {64, 128}, a K/V
+ *   slice (Lk * d elements) of more than INT32_MAX bytes, or more than 2^30
+ *   (batch x head, 128-row query tile) pairs.
  */
 ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt,
                   int32_t B, int32_t H, int32_t Lq, int32_t Lk, int32_t d,
@@ -229,9 +231,10 @@ ra_status ra_bwd_prep(const void* out, const void* dout, ra_dtype dt, int32_t B,
  * accumulation). The two kernels run one after the other on `stream`.
  * Errors: those of ra_step_gqa, RA_ERR_INVALID_ARG for a null dout, lse, delta or
  *   accumulator, unknown flags, both RA_BWD_NO_DQ and RA_BWD_NO_DKV, or an
- *   accumulator overlapping an input or
- *   another accumulator; RA_ERR_UNSUPPORTED for dt != RA_BF16 or more than
- *   2^30 (K/V head, 256-key tile) pairs.
+ *   accumulator overlapping an input or another accumulator;
+ *   RA_ERR_UNSUPPORTED for dt != RA_BF16, a local query slice (Lq * d
+ *   elements) of more than INT32_MAX bytes, or more than 2^30 (K/V head,
+ *   256-key tile) pairs.
  */
 ra_status ra_step_bwd(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, const float* delta, ra_dtype dt,

@@ -209,6 +209,16 @@ def test_step_bwd_refuses_grids_past_32_bits(lib):
                            ctypes.byref(b), 1, 0.1, 3, p[6], p[7], p[8], None) == INV
 
 
+def test_step_bwd_refuses_query_slices_past_32_bit_bytes(lib):
+    # 2^23 local queries at d=128 bf16 are 2^31 bytes per slice: past the
+    # 32-bit byte size of the buffer resource the dK/dV kernel streams them with
+    Lq = 1 << 23
+    a, b = _lib.segs([(0, Lq)]), _lib.segs([(0, 64)])
+    p = [(i + 1) << 48 for i in range(9)]
+    assert lib.ra_step_bwd(p[0], p[1], p[2], p[3], p[4], p[5], 1, 1, 1, 1, Lq, 64, 128,
+                           ctypes.byref(a), ctypes.byref(b), 1, 0.1, 3, p[6], p[7], p[8], None) == UNS
+
+
 def test_bwd_prep_validation(lib):
     p = lib.ra_bwd_prep
     assert p(None, ptr(1), 1, 1, 1, 64, 128, ptr(2), None) == INV
