@@ -175,7 +175,6 @@ def time_backward(w, rank, q, segs, kv, out, lse, reps, warmup=3):
     fl = 2.0 * sum(ring_flop(w, rank, segs))
     return {"workload": f"{w.name} rank {rank}, {w.P} backward ring steps", "ms": ms,
             "TFLOP/s": fl / ms / 1e9, "mfma_frac": fl / ms / 1e-3 / PEAK_BF16_DENSE,
-            "dkv_side_stream": w.Hkv != w.H,
             "flop": fl, "flop_convention": "8*d per visible pair (the dV, dP, dQ and dK products); "
             "the kernels execute 14*d (scores and dP are formed in both the dQ and the dK/dV kernel)"}
 

@@ -147,24 +147,39 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
       (void)klo;
       need_mask = need_mask || khi > w_qlo;
     }
+    // the products of both 32-key halves first, so that the second half's
+    // run on the matrix core while the first half's weights are formed
+    f32x16 s[2], dpv[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      f32x16 s = f32x16{}, dpv = f32x16{};
+      s[st] = f32x16{};
+      dpv[st] = f32x16{};
 #pragma unroll
       for (int ksi = 0; ksi < KS; ++ksi) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(kt, st, ksi, l32, h), qf[ksi], s, 0, 0, 0);
-        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vt, st, ksi, l32, h), df[ksi], dpv, 0, 0, 0);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(kt, st, ksi, l32, h), qf[ksi], s[st], 0, 0, 0);
+        dpv[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vt, st, ksi, l32, h), df[ksi], dpv[st], 0, 0, 0);
       }
+    }
+    // masked scores become -inf (weight exactly 0) in one block per tile, so
+    // that the exponentials below are straight-line code
+    if (need_mask) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t kr = kt0 + 32 * st + acc_row(r, h);
+          const bool vis = kr < Lk && (!CAUSAL || seg_pos(ks, kr) <= qpos);
+          s[st][r] = vis ? s[st][r] : kNegInf;
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
       f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[r], c_log2, -lse2));
-        if (need_mask) {
-          const int32_t kr = kt0 + 32 * st + acc_row(r, h);
-          const bool vis = kr < Lk && (!CAUSAL || seg_pos(ks, kr) <= qpos);
-          p = vis ? p : 0.f;
-        }
-        ds[r] = p * (dpv[r] - dlt);
+        // c_log2 > 0 and lse2 is finite or +inf, so a -inf score gives p = 0
+        const float p = fast_exp2(__builtin_fmaf(s[st][r], c_log2, -lse2));
+        ds[r] = p * (dpv[st][r] - dlt);
       }
       bf16x8 b0, b1;
       pack_b(ds, b0, b1);

@@ -148,7 +148,7 @@ def run_bwd(q: torch.Tensor,
             scale: Optional[float] = None,
             order: Optional[List[int]] = None,
             dkv: Optional[List[Tuple[torch.Tensor, torch.Tensor]]] = None,
-            overlap: Optional[bool] = None):
+            overlap: bool = False):
     """Backward pass of rank `rank`'s share: P backward block steps.
 
     The ring passes the K/V blocks again in the backward pass (k8ai
@@ -164,9 +164,7 @@ def run_bwd(q: torch.Tensor,
     overlap    run the dK/dV half of every step on a second stream, beside the
                chain of dQ halves on the current stream (each block's dK/dV
                depends on no other step), and make the current stream wait for
-               it before returning. None: only with grouped K/V heads, where
-               the dK/dV kernel is a single round of workgroups and the
-               causal imbalance of the diagonal step would leave CUs idle
+               it before returning; the gradients are bitwise the same
     returns (dq [B, H, Lq, d] fp32, dkv)
     """
     P = len(kv_blocks)
@@ -186,8 +184,6 @@ def run_bwd(q: torch.Tensor,
     delta = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
     _lib.ra_bwd_prep(out, dout, delta, stream=stream)
     dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device=dev)
-    if overlap is None:
-        overlap = kv_blocks[0][0].shape[1] != H
     side = None
     if overlap:
         side = torch.cuda.Stream(dev)
