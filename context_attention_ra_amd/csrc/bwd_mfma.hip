@@ -337,6 +337,16 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
         dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(dt, st, ksi, l32, h),
                                                       row_operand<D>(vw, w & 1, ksi, l32, h), dpv, 0, 0, 0);
       }
+      // masked scores become -inf (weight exactly 0) in one block, so that
+      // the exponentials below are straight-line code
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t q = qt0 + 32 * st + acc_row(r, h);
+          const bool vis = q < Lq && seg_pos(qs, q) >= kpos;
+          s[r] = vis ? s[r] : kNegInf;
+        }
+      }
       f32x16 p, ds;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -346,12 +356,8 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * i + j;
-          float pv = fast_exp2(__builtin_fmaf(s[r], c_log2, -l4[j]));
-          if (need_mask) {
-            const int32_t q = qt0 + rb + j;
-            const bool vis = q < Lq && seg_pos(qs, q) >= kpos;
-            pv = vis ? pv : 0.f;
-          }
+          // c_log2 > 0 and the row's lse is finite or +inf: a -inf score gives 0
+          const float pv = fast_exp2(__builtin_fmaf(s[r], c_log2, -l4[j]));
           p[r] = pv;
           ds[r] = pv * (dpv[r] - d4[j]);
         }
