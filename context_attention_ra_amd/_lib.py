@@ -143,10 +143,36 @@ def _shape(name, t, want):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(want)}")
 
 
+F32 = torch.float32
+
+
+def _dtypes(ref, *named):
+    """Every tensor must have the dtype the C call assumes.
+
+    The C ABI sees bare pointers and derives every byte count from one dtype
+    argument, so a tensor of another dtype would be read or written past its
+    end. named: (name, tensor or None, required dtype)."""
+    _dtype(ref)
+    for name, t, dt in named:
+        if t is not None and t.dtype != dt:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {dt}")
+
+
+def _on_gpu(ref, *tensors):
+    """Every tensor must sit on `ref`'s GPU: the kernels would take a host
+    pointer, or another device's, for one of their own."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors passed to libra must be on a GPU, got {ref.device}")
+    for t in tensors:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"tensor on {t.device}, expected {ref.device}")
+
+
 def _check_step(q, k, v, o_acc, m, l, grouped=True):
     """The sizes the C call derives from q and k must describe every buffer it touches."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be [B, H, L, d]")
+    _dtypes(q, ("k", k, q.dtype), ("v", v, q.dtype), ("o_acc", o_acc, F32), ("m", m, F32), ("l", l, F32))
     B, H, Lq, d = q.shape
     H_kv, Lk = k.shape[1], k.shape[2]
     if k.shape[0] != B or k.shape[3] != d or H_kv < 1 or H % H_kv != 0 or (not grouped and H_kv != H):
@@ -160,6 +186,7 @@ def _check_step(q, k, v, o_acc, m, l, grouped=True):
 def ra_step(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, init=False, stream=None):
     """ra_step; with fewer K/V heads than query heads (k.shape[1] < q.shape[1]) ra_step_gqa."""
     _check_step(q, k, v, o_acc, m, l)
+    _on_gpu(q, k, v, o_acc, m, l)
     B, H, Lq, d = q.shape
     H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
@@ -176,8 +203,10 @@ def ra_step_final(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, out, lse
                   init=False, stream=None):
     """ra_step_final; with fewer K/V heads than query heads ra_step_final_gqa."""
     _check_step(q, k, v, o_acc, m, l)
+    _dtypes(q, ("out", out, q.dtype), ("lse", lse, F32))
     _shape("out", out, q.shape)
     _shape("lse", lse, q.shape[:3])
+    _on_gpu(q, k, v, o_acc, m, l, out, lse)
     B, H, Lq, d = q.shape
     H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
@@ -194,8 +223,10 @@ def ra_step_final(q, k, v, q_segs, kv_segs, causal, scale, o_acc, m, l, out, lse
 
 def ra_bwd_prep(out, dout, delta, stream=None):
     B, H, L, d = out.shape
+    _dtypes(out, ("dout", dout, out.dtype), ("delta", delta, F32))
     _shape("dout", dout, out.shape)
     _shape("delta", delta, (B, H, L))
+    _on_gpu(out, dout, delta)
     _check("ra_bwd_prep", load().ra_bwd_prep(_p(out), _p(dout), _dtype(out), B, H, L, d, _p(delta),
                                              _s(stream)))
 
@@ -206,9 +237,11 @@ def ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs, causal, scale, dq, d
     if parts not in ("both", "dq", "dkv"):
         raise ValueError(f"parts must be 'both', 'dq' or 'dkv', not {parts!r}")
     _check_step(q, k, v, dq, lse, delta)
+    _dtypes(q, ("dout", dout, q.dtype), ("dk", dk, F32), ("dv", dv, F32))
     _shape("dout", dout, q.shape)
     _shape("dk", dk, k.shape)
     _shape("dv", dv, k.shape)
+    _on_gpu(q, k, v, dout, lse, delta, dq, dk, dv)
     B, H, Lq, d = q.shape
     H_kv, Lk = k.shape[1], k.shape[2]
     qs, ks = segs(q_segs), segs(kv_segs)
@@ -222,18 +255,23 @@ def ra_step_bwd(q, k, v, dout, lse, delta, q_segs, kv_segs, causal, scale, dq, d
 
 def ra_finalize(o_acc, m, l, out, lse=None, stream=None):
     B, H, L, d = o_acc.shape
+    _dtypes(out, ("o_acc", o_acc, F32), ("m", m, F32), ("l", l, F32), ("lse", lse, F32))
     for n, t, want in (("m", m, (B, H, L)), ("l", l, (B, H, L)), ("out", out, o_acc.shape),
                        ("lse", lse, (B, H, L))):
         _shape(n, t, want)
+    _on_gpu(o_acc, m, l, out, lse)
     _check("ra_finalize", load().ra_finalize(_p(o_acc), _p(m), _p(l), B, H, L, d, _p(out),
                                              _dtype(out), _p(lse), _s(stream)))
 
 
 def ra_merge_lse(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
     B, H, L, d = o_a.shape
+    _dtypes(o_a, ("o_b", o_b, o_a.dtype), ("o_out", o_out, o_a.dtype), ("lse_a", lse_a, F32),
+            ("lse_b", lse_b, F32), ("lse_out", lse_out, F32))
     for n, t, want in (("o_b", o_b, o_a.shape), ("o_out", o_out, o_a.shape), ("lse_a", lse_a, (B, H, L)),
                        ("lse_b", lse_b, (B, H, L)), ("lse_out", lse_out, (B, H, L))):
         _shape(n, t, want)
+    _on_gpu(o_a, lse_a, o_b, lse_b, o_out, lse_out)
     _check("ra_merge_lse", load().ra_merge_lse(_p(o_a), _p(lse_a), _p(o_b), _p(lse_b),
                                                _dtype(o_a), B, H, L, d, _p(o_out),
                                                _p(lse_out), _s(stream)))
@@ -241,20 +279,24 @@ def ra_merge_lse(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
 
 def ra_factored_spatial(q, k, v, T, S_sp, scale, out, lse=None, stream=None):
     B, H, N, d = q.shape
+    _dtypes(q, ("k", k, q.dtype), ("v", v, q.dtype), ("out", out, q.dtype), ("lse", lse, F32))
     if N != T * S_sp:
         raise ValueError("q.shape[2] must equal T * S_sp")
     for n, t, want in (("k", k, q.shape), ("v", v, q.shape), ("out", out, q.shape), ("lse", lse, (B, H, N))):
         _shape(n, t, want)
+    _on_gpu(q, k, v, out, lse)
     _check("ra_factored_spatial", load().ra_factored_spatial(
         _p(q), _p(k), _p(v), _dtype(q), B, H, T, S_sp, d, float(scale), _p(out), _p(lse), _s(stream)))
 
 
 def ra_factored_temporal(q, k, v, T, S_sp, scale, out, lse=None, stream=None):
     B, H, N, d = q.shape
+    _dtypes(q, ("k", k, q.dtype), ("v", v, q.dtype), ("out", out, q.dtype), ("lse", lse, F32))
     if N != T * S_sp:
         raise ValueError("q.shape[2] must equal T * S_sp")
     for n, t, want in (("k", k, q.shape), ("v", v, q.shape), ("out", out, q.shape), ("lse", lse, (B, H, N))):
         _shape(n, t, want)
+    _on_gpu(q, k, v, out, lse)
     _check("ra_factored_temporal", load().ra_factored_temporal(
         _p(q), _p(k), _p(v), _dtype(q), B, H, T, S_sp, d, float(scale), _p(out), _p(lse), _s(stream)))
 
@@ -264,6 +306,7 @@ def ra_kv_pass(k_src, v_src, k_dst, v_dst, stream=None):
     for t in (v_src, k_dst, v_dst):
         if t.numel() * t.element_size() != nbytes:
             raise ValueError("ra_kv_pass: all four buffers must have the same size")
+    _on_gpu(k_src, v_src, k_dst, v_dst)
     _check("ra_kv_pass", load().ra_kv_pass(_p(k_src), _p(v_src), _p(k_dst), _p(v_dst),
                                            nbytes, _s(stream)))
 
@@ -276,6 +319,7 @@ def ra_copy_rows(src, src_row0, dst, dst_row0, nrows, src_slice0=0, dst_slice0=0
         raise ValueError("ra_copy_rows: source and destination need the same dtype and row width")
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("tensors passed to libra must be contiguous")
+    _on_gpu(src, dst)
     sr, dr = src.shape[-2], dst.shape[-2]
     ns, nd = src.numel() // (sr * src.shape[-1]), dst.numel() // (dr * dst.shape[-1])
     if nslices is None:

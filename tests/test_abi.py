@@ -285,3 +285,75 @@ def test_ring_drivers_refuse_bad_block_orders():
             ring.run(q, segs[0], kv, segs, 0, True, order=order)
         with pytest.raises(ValueError):
             ring.run_bwd(q, segs[0], kv, segs, 0, True, q, torch.zeros((1, 1, 64)), q, order=order)
+
+
+def test_binding_checks_dtypes_and_devices_before_any_library_call(monkeypatch):
+    # The C calls derive every byte count from one dtype argument and cannot
+    # tell host pointers from device ones: the binding must refuse mismatched
+    # dtypes and tensors off the GPU before the library is even loaded.
+    import torch
+
+    def no_call(*a, **k):
+        raise AssertionError("the library was reached")
+
+    monkeypatch.setattr(_lib, "load", no_call)
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros((1, 2, 64, 64), dtype=bf)
+    st = [torch.zeros((1, 2, 64, 64)), torch.zeros((1, 2, 64)), torch.zeros((1, 2, 64))]
+    segs = ([(0, 64)], [(0, 64)], True, 0.1)
+    with pytest.raises(TypeError):  # fp32 queries with bf16 keys: K/V read at twice their size
+        _lib.ra_step(q.float(), q, q, *segs, *st)
+    with pytest.raises(TypeError):
+        _lib.ra_step(q, q, q.float(), *segs, *st)
+    with pytest.raises(TypeError):  # a bf16 running state would take fp32 stores
+        _lib.ra_step(q, q, q, *segs, st[0].to(bf), st[1], st[2])
+    with pytest.raises(TypeError):
+        _lib.ra_step(q, q, q, *segs, st[0], st[1].to(bf), st[2])
+    with pytest.raises(TypeError):  # fp16 is not a library dtype
+        _lib.ra_step(q.half(), q.half(), q.half(), *segs, *st)
+    with pytest.raises(ValueError, match="GPU"):  # right dtypes, host memory
+        _lib.ra_step(q, q, q, *segs, *st)
+    with pytest.raises(TypeError):
+        _lib.ra_step_final(q, q, q, *segs, *st, q.float(), st[1])
+    with pytest.raises(TypeError):
+        _lib.ra_step_final(q, q, q, *segs, *st, q, st[1].to(bf))
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.ra_step_final(q, q, q, *segs, *st, q, st[1])
+    lse, delta = st[1], st[2]
+    with pytest.raises(TypeError):  # gradient accumulators are fp32
+        _lib.ra_step_bwd(q, q, q, q, lse, delta, *segs, st[0], st[0].to(bf), st[0])
+    with pytest.raises(TypeError):
+        _lib.ra_step_bwd(q, q, q, q.float(), lse, delta, *segs, st[0], st[0], st[0])
+    with pytest.raises(TypeError):
+        _lib.ra_step_bwd(q, q, q, q, lse, delta, *segs, st[0].to(bf), st[0], st[0])
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.ra_step_bwd(q, q, q, q, lse, delta, *segs, st[0], st[0], st[0])
+    with pytest.raises(TypeError):
+        _lib.ra_bwd_prep(q, q.float(), delta)
+    with pytest.raises(TypeError):
+        _lib.ra_bwd_prep(q, q, delta.to(bf))
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.ra_bwd_prep(q, q, delta)
+    with pytest.raises(TypeError):
+        _lib.ra_finalize(st[0], st[1], st[2], q.half())
+    with pytest.raises(TypeError):
+        _lib.ra_finalize(st[0].to(bf), st[1], st[2], q)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.ra_finalize(st[0], st[1], st[2], q, lse)
+    with pytest.raises(TypeError):
+        _lib.ra_merge_lse(q, lse, q.float(), lse, q, lse)
+    with pytest.raises(TypeError):
+        _lib.ra_merge_lse(q, lse, q, lse.to(bf), q, lse)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.ra_merge_lse(q, lse, q, lse, torch.empty_like(q), torch.empty_like(lse))
+    for fn in (_lib.ra_factored_spatial, _lib.ra_factored_temporal):
+        with pytest.raises(TypeError):
+            fn(q, q.float(), q, 4, 16, 0.1, torch.empty_like(q))
+        with pytest.raises(TypeError):
+            fn(q, q, q, 4, 16, 0.1, torch.empty_like(q), lse.to(bf))
+        with pytest.raises(ValueError, match="GPU"):
+            fn(q, q, q, 4, 16, 0.1, torch.empty_like(q), lse)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.ra_kv_pass(q, q, torch.empty_like(q), torch.empty_like(q))
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.ra_copy_rows(q, 0, torch.empty_like(q), 0, 8)

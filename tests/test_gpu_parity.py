@@ -391,11 +391,13 @@ def test_merge_lse_parity(gpu_lib, dt, d):
     go, gl = oo.float().cpu().double().numpy(), lo.cpu().double().numpy()
     both = ~np.isfinite(rl)
     assert np.array_equal(both, ~np.isfinite(gl))
-    tol = 2e-2 if dt == torch.bfloat16 else 1e-5
+    # the stated output bounds: bf16 2e-2 max-abs and 1e-2 mean-relative; fp32
+    # 1e-5 max-abs (tighter than 1e-4: one rescale and one add per element)
+    tol, rel_tol = (2e-2, 1e-2) if dt == torch.bfloat16 else (1e-5, 1e-4)
     mx, mr = compare(go, ro)
     lm, _ = compare(np.where(both, 0, gl), np.where(both, 0, rl))
     print(f"merge {dt} d{d}: max_abs={mx:.3e} mean_rel={mr:.3e} lse={lm:.3e}", flush=True)
-    assert mx <= tol and lm <= 1e-5
+    assert mx <= tol and mr <= rel_tol and lm <= 1e-5
 
 
 def test_invalid_arguments_raise_before_launch(gpu_lib):
