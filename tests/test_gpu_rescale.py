@@ -91,11 +91,12 @@ def test_rescale_across_steps_noncausal_ring(gpu_lib):
     # blocks visited in rising order: each step's scores outgrow the reference
     # value the previous step stored, so the rescale starts from a state read
     # back from memory (the checkpointed m of the last step)
-    w = configs.RingWorkload(901, "rising-noncausal-4k-cp4", B=1, H=2, d=128, S=4096, P=4,
+    w = configs.RingWorkload(903, "stair-noncausal-4k-cp4", B=1, H=2, d=128, S=4096, P=4,
                              split="contiguous", causal=False, dtype=torch.bfloat16)
     order = [0, 1, 2, 3]
     banner(f"{w.name}: rank 0, blocks in rising order {order}")
-    q, k, v = rising.rising_global(w.wid, w.B, w.H, w.Hkv, w.S, w.d, q_gain=8.0, lo=0.25, hi=4.0)
+    q, k, v = rising.rising_global(w.wid, w.B, w.H, w.Hkv, w.S, w.d, q_gain=4.0,
+                                   gains=rising.stair_gains(w.S, w.P))
     segs = [layout.split(w.split, w.S, w.P, t) for t in range(w.P)]
     pos = [np.arange(s, s + n) for sg in segs for s, n in sg]
     # every row must rescale at some step after the first
