@@ -204,6 +204,61 @@ def time_variants(w, rank, q, segs, kv, reps, warmup=2):
     return res
 
 
+def time_small_ring(dev, reps=50):
+    """Whole ring pass of the causal 4K two-rank share (rank 0): two steps and
+    the block pass, too small to fill the chip (launch-bound); reported for
+    completeness beside the 32K share."""
+    w = configs.CAUSAL_2RANK
+    q, segs, kv = make_ring_inputs(w, 0, dev)
+    bufs = [(torch.empty_like(kv[0][0]), torch.empty_like(kv[0][1])) for _ in range(2)]
+    side = torch.cuda.Stream(dev)
+    st = ring.RingState(w.B, w.H, w.L, w.d, dev)
+    out, lse = torch.empty_like(q), torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+    ms = time_kernel(lambda: ring.run(q, segs[0], kv, segs, 0, w.causal, scale=w.scale, out=out, lse=lse,
+                                      state=st, bufs=bufs, copy_stream=side), reps, warmup=10)
+    fl = float(sum(ring_flop(w, 0, segs)))
+    return {"workload": f"{w.name} rank 0, whole ring pass ({w.P} steps)", "ms": ms, "TFLOP/s": fl / ms / 1e9,
+            "mfma_frac": fl / ms / 1e-3 / PEAK_BF16_DENSE, "flop": fl}
+
+
+def time_video_steps(dev, reps=2):
+    """Two ring steps of the video DiT share (rank 0: 54,000 local queries,
+    two non-causal 54,000-token K/V blocks, 32 heads, d = 128): the first with
+    RA_STEP_INIT, the second reading the state back, as in the ring. Inputs
+    are seeded N(0,1) draws made on the GPU (timing only; the parity tests use
+    the oracle's seeded rows)."""
+    w = configs.VIDEO_DIT_CP8
+    g = torch.Generator(device=dev).manual_seed(20263)
+    L = w.L
+    q = torch.randn((w.B, w.H, L, w.d), generator=g, device=dev).to(w.dtype)
+    blocks = [tuple(torch.randn((w.B, w.H, L, w.d), generator=g, device=dev).to(w.dtype) for _ in range(2))
+              for _ in range(2)]
+    st = ring.RingState(w.B, w.H, L, w.d, dev)
+    segs = [layout.split(w.split, w.S, w.P, t, S_sp=w.S_sp) for t in range(w.P)]
+    order = layout.ring_order(0, w.P)[:2]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * reps)]
+
+    def two_steps(events):
+        for s, t in enumerate(order):
+            k, v = blocks[s]
+            events[s][0].record()
+            _lib.ra_step(q, k, v, segs[0], segs[t], False, w.scale, st.o, st.m, st.l, init=(s == 0))
+            events[s][1].record()
+
+    two_steps(ev[:2])  # warm-up
+    torch.cuda.synchronize()
+    for r in range(reps):
+        two_steps(ev[2 * r:2 * r + 2])
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.mean(per))
+    fl = sizing.attention_flop(L * L, w.d, w.B * w.H)
+    assert torch.isfinite(st.l).all()
+    return {"workload": f"{w.name} rank 0, ring steps 0 and 1 (init, then state read back)", "ms_per_step": ms,
+            "ms_per_step_each": per, "TFLOP/s": fl / ms / 1e9, "mfma_frac": fl / ms / 1e-3 / PEAK_BF16_DENSE,
+            "flop_per_step": fl, "timing": f"HIP events around each ra_step launch, {reps} reps after one warm-up"}
+
+
 def legs(w, q, dev, reps):
     out = {}
     # LSE merge of two normalised partials of this workload's shape (bf16)
@@ -266,6 +321,24 @@ def legs(w, q, dev, reps):
                                 "plain_stream_GB/s": pbytes / plain / 1e6,
                                 "plain_stream": "torch.addcmul of q, k, v (3 reads + 1 write)",
                                 "caches": "evicted by reading 1 GiB before each rep"}
+    # longer clips (Day 83 post: 48 frames of 900 tokens; 120 frames, one of
+    # 8 devices' 450 spatial positions after the re-split), 32 heads, d = 128
+    g2 = torch.Generator(device=dev).manual_seed(20264)
+    for T, S_sp in ((48, 900), (120, 450)):
+        shape = (1, 32, T * S_sp, 128)
+        ql, kl, vl = (torch.randn(shape, generator=g2, device=dev).to(torch.bfloat16) for _ in range(3))
+        ol = torch.empty_like(ql)
+        ll = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+        ms = evicted_ms(lambda: _lib.ra_factored_temporal(ql, kl, vl, T, S_sp, 128 ** -0.5, ol, ll))
+        plain = evicted_ms(lambda: torch.addcmul(ql, kl, vl, out=ol))
+        nbytes = 4 * ql.numel() * 2 + ll.numel() * 4
+        out[f"factored_temporal_{T}x{S_sp}"] = {
+            "workload": f"{T} frames x {S_sp} positions, H=32, d=128, bf16", "ms": ms,
+            "GB/s": nbytes / ms / 1e6, "hbm_frac": nbytes / ms / 1e-3 / PEAK_HBM,
+            "plain_stream_GB/s": 4 * ql.numel() * 2 / plain / 1e6,
+            "TFLOP/s": sizing.attention_flop(T * T * S_sp, 128, 32) / ms / 1e9,
+            "caches": "evicted by reading 1 GiB before each rep"}
+        del ql, kl, vl, ol, ll
     return out
 
 
@@ -395,6 +468,19 @@ def main():
         "ring_ms_per_pass": ms_per_step,
         "kernel_share_of_pass": float(kms.sum(axis=1).mean()) / ms_per_step,
     }
+    # the same pass with each block passed on the compute stream before its
+    # step (no overlap), so that the side stream's effect is in the record
+    cmp_prefetch = args.no_prefetch  # the mode the main measurement did not use
+    log(f"[bench] ring pass with prefetch={cmp_prefetch} for comparison")
+    n2 = max(4, args.steps // 2)
+    wall2, kms2, _, _ = time_ring(w, args.rank, q, segs, kv, n2, 3, cmp_prefetch)
+    ms2 = wall2 / n2 * 1e3
+    tag = "prefetch" if cmp_prefetch else "no_prefetch"
+    rec["ring_ms_per_pass_" + tag] = ms2
+    rec["ring_kernel_ms_mean_" + tag] = float(kms2.mean())
+    with_pf, without_pf = (ms2, ms_per_step) if cmp_prefetch else (ms_per_step, ms2)
+    # share of the serial pass time that passing the blocks on the side stream saves
+    rec["prefetch_saving"] = (without_pf - with_pf) / without_pf
     if not args.no_legs:
         log("[bench] legs: merge, factored spatial, factored temporal")
         rec["legs"] = legs(w, q, dev, reps=20)
@@ -403,6 +489,9 @@ def main():
             rec["legs"]["backward"] = time_backward(w, args.rank, q, segs, kv, out, lse, reps=10)
         log("[bench] leg: all-gather and all-to-all on heads")
         rec["legs"]["variants"] = time_variants(w, args.rank, q, segs, kv, reps=5)
+        log("[bench] legs: the other ring workloads (4K two-rank ring, video DiT share steps)")
+        rec["legs"]["ring_causal_4k_cp2"] = time_small_ring(dev)
+        rec["legs"]["video_dit_432k_cp8_steps"] = time_video_steps(dev)
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_budget:.0f} s")
         rec["cpu_baseline"] = cpu_baseline(w, args.rank, segs, args.cpu_budget)

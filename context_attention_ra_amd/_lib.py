@@ -25,7 +25,7 @@ RA_BWD_NO_DKV = 8
 
 # every symbol include/ra.h declares
 EXPORTS = ("ra_step", "ra_finalize", "ra_step_final", "ra_step_gqa", "ra_step_final_gqa",
-           "ra_bwd_prep", "ra_step_bwd", "ra_copy_rows",
+           "ra_bwd_prep", "ra_step_bwd", "ra_copy_rows", "ra_add_rows",
            "ra_merge_lse", "ra_factored_spatial",
            "ra_factored_temporal", "ra_kv_pass", "ra_status_string",
            "ra_last_hip_error", "ra_version")
@@ -72,6 +72,8 @@ _SIGS = {
     "ra_kv_pass": (_i32, [_vp, _vp, _vp, _vp, _sz, _vp]),
     "ra_copy_rows": (_i32, [_vp, ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64,
                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp]),
+    "ra_add_rows": (_i32, [_vp, ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64,
+                           ctypes.c_int64, ctypes.c_int64, _i32, _vp]),
     "ra_status_string": (ctypes.c_char_p, [_i32]),
     "ra_last_hip_error": (_i32, []),
     "ra_version": (_i32, []),
@@ -331,3 +333,25 @@ def ra_copy_rows(src, src_row0, dst, dst_row0, nrows, src_slice0=0, dst_slice0=0
     dp = dst.data_ptr() + dst_slice0 * dr * row_bytes
     _check("ra_copy_rows", load().ra_copy_rows(sp, sr, src_row0, dp, dr, dst_row0, nslices, nrows,
                                                row_bytes, _s(stream)))
+
+
+def ra_add_rows(src, src_row0, dst, dst_row0, nrows, src_slice0=0, dst_slice0=0, nslices=None,
+                stream=None):
+    """dst rows [dst_row0, +nrows) += src rows [src_row0, +nrows) of slices
+    src_slice0.. / dst_slice0.. of two fp32 [..., rows, d] tensors."""
+    _dtypes(src, ("src", src, F32), ("dst", dst, F32))
+    if src.shape[-1] != dst.shape[-1]:
+        raise ValueError("ra_add_rows: source and destination need the same row width")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("tensors passed to libra must be contiguous")
+    sr, dr, d = src.shape[-2], dst.shape[-2], src.shape[-1]
+    ns, nd = src.numel() // (sr * d), dst.numel() // (dr * d)
+    if nslices is None:
+        nslices = ns - src_slice0
+    if src_slice0 < 0 or dst_slice0 < 0 or src_slice0 + nslices > ns or dst_slice0 + nslices > nd:
+        raise ValueError("ra_add_rows: slice range outside a tensor")
+    _on_gpu(src, dst)
+    sp = src.data_ptr() + src_slice0 * sr * d * 4
+    dp = dst.data_ptr() + dst_slice0 * dr * d * 4
+    _check("ra_add_rows", load().ra_add_rows(sp, sr, src_row0, dp, dr, dst_row0, nslices, nrows, d,
+                                             _s(stream)))

@@ -15,8 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libra.so")
 
-SOURCES = ["step_mfma.hip", "step_f32.hip", "finalize_merge.hip", "temporal.hip", "bwd_mfma.hip",
-           "ra_abi.cpp"]
+SOURCES = ["step_mfma.hip", "step_f32.hip", "finalize_merge.hip", "temporal.hip", "temporal_long.hip", "rows.hip",
+           "bwd_mfma.hip", "ra_abi.cpp"]
 
 # gfx950 only; packed fp32 VALU ops are disabled for every HIP translation unit.
 HIPCC_FLAGS = [

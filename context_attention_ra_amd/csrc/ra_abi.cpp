@@ -8,6 +8,7 @@
 
 #include "ra_bwd.h"
 #include "ra_launch.h"
+#include "ra_stream_launch.h"
 
 namespace {
 
@@ -319,8 +320,15 @@ ra_status ra_factored_temporal(const void* q, const void* k, const void* v, ra_d
                                void* out, float* lse, hipStream_t stream) {
   const ra_status st = factored_check(q, k, v, dt, B, H, T, S_sp, d, scale, out, lse);
   if (st != RA_OK) return st;
-  if (T > 16) return RA_ERR_UNSUPPORTED;
-  return hip_fail(ra::launch_temporal_bf16(q, k, v, B * H, T, S_sp, d, scale, out, lse, stream));
+  if (T > 128) return RA_ERR_UNSUPPORTED;
+  // the long-clip kernel addresses the T rows of a position from the start of
+  // its (batch, head) slice with 32-bit byte offsets
+  if (T > 16 && (int64_t)T * S_sp * d * (int64_t)esize(dt) > (int64_t)INT32_MAX) return RA_ERR_UNSUPPORTED;
+  // up to 16 frames: one wave per problem; longer clips: one workgroup per
+  // problem with the K/V frames staged in LDS
+  if (T <= 16)
+    return hip_fail(ra::launch_temporal_bf16(q, k, v, B * H, T, S_sp, d, scale, out, lse, stream));
+  return hip_fail(ra::launch_temporal_long_bf16(q, k, v, B * H, T, S_sp, d, scale, out, lse, stream));
 }
 
 ra_status ra_kv_pass(const void* k_src, const void* v_src, void* k_dst, void* v_dst, size_t bytes,
@@ -352,6 +360,23 @@ ra_status ra_copy_rows(const void* src, int64_t src_slice_rows, int64_t src_row0
                                    (const char*)src + src_row0 * row_bytes, sp,
                                    (size_t)nrows * row_bytes, (size_t)nslices,
                                    hipMemcpyDeviceToDevice, stream));
+}
+
+ra_status ra_add_rows(const float* src, int64_t src_slice_rows, int64_t src_row0, float* dst,
+                      int64_t dst_slice_rows, int64_t dst_row0, int64_t nslices, int64_t nrows,
+                      int32_t d, hipStream_t stream) {
+  if (nrows == 0) return RA_OK;
+  if (!src || !dst || nslices <= 0 || nrows < 0 || d <= 0 || d % 4 != 0) return RA_ERR_INVALID_ARG;
+  if (src_row0 < 0 || dst_row0 < 0 || src_row0 + nrows > src_slice_rows ||
+      dst_row0 + nrows > dst_slice_rows)
+    return RA_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return RA_ERR_INVALID_ARG;
+  const size_t rb = (size_t)d * 4;
+  const Range rs = span((const char*)src + src_row0 * rb, (size_t)src_slice_rows * rb * (nslices - 1) + nrows * rb);
+  const Range rd = span((const char*)dst + dst_row0 * rb, (size_t)dst_slice_rows * rb * (nslices - 1) + nrows * rb);
+  if (overlap(rs, rd)) return RA_ERR_INVALID_ARG;
+  return hip_fail(ra::launch_add_rows(src, src_slice_rows, src_row0, dst, dst_slice_rows, dst_row0,
+                                      nslices, nrows, d, stream));
 }
 
 const char* ra_status_string(ra_status s) {

@@ -1,9 +1,11 @@
 """The alternatives to the ring that the pages name, one rank's share on one GPU.
 
 * All-gather: the Ultralytics glossary ("How Context Parallelism Works") lists
-  all-gather next to ring-based exchange of K/V blocks. Every rank gathers all
-  K/V blocks at their global positions, then attends its local queries to the
-  whole sequence in one step.
+  all-gather and reduce-scatter next to ring-based exchange of K/V blocks.
+  Every rank gathers all K/V blocks at their global positions, then attends
+  its local queries to the whole sequence in one step. In the backward pass
+  each rank's gradient of the gathered K/V covers every position; a
+  reduce-scatter sums those over the ranks into the rows each rank owns.
 * All-to-all on heads: in the scheme of the k8ai page ("An alternative:
   all-to-all on heads") the ranks trade their token ranges for head groups
   before the attention and trade back after it, so the number of heads bounds
@@ -77,6 +79,62 @@ def run_allgather(q: torch.Tensor, q_segs: Segs,
     _lib.ra_step_final(q, kg, vg, q_segs, [(0, S)], causal, scale, st.o, st.m, st.l, out, lse,
                        init=True, stream=stream)
     return out, lse
+
+
+def allgather_bwd(q: torch.Tensor, q_segs: Segs,
+                  kv_blocks: Sequence[Tuple[torch.Tensor, torch.Tensor]], kv_segs: Sequence[Segs],
+                  causal: bool, out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                  scale: Optional[float] = None):
+    """Backward pass of one rank's share under all-gather.
+
+    The rank's queries saw the gathered K/V, so its backward step yields dQ
+    for its own rows and this rank's contribution to dK and dV at every global
+    position; ``reduce_scatter`` then sums those contributions over the ranks
+    into the rows each rank owns (the adjoint of the gather).
+
+    out, lse   the rank's forward output and lse (``run_allgather``)
+    dout       upstream gradient of `out`
+    returns (dq [B, H, Lq, d] fp32, dk, dv [B, H_kv, S, d] fp32, global order)
+    """
+    B, H, Lq, d = q.shape
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    stream = torch.cuda.current_stream(q.device)
+    kg, vg = gather_kv(kv_blocks, kv_segs, stream=stream)
+    S = kg.shape[2]
+    delta = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    _lib.ra_bwd_prep(out, dout, delta, stream=stream)
+    dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty(kg.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    _lib.ra_step_bwd(q, kg, vg, dout, lse, delta, q_segs, [(0, S)], causal, scale, dq, dk, dv,
+                     init_dq=True, init_dkv=True, stream=stream)
+    return dq, dk, dv
+
+
+def reduce_scatter(partials: Sequence[torch.Tensor], segs: Sequence[Segs], stream=None) -> List[torch.Tensor]:
+    """Reduce-scatter over the ranks: rank t receives the sum of every rank's
+    partial at the global positions it owns.
+
+    partials  P fp32 tensors [B, Hb, S, d] in global position order (one per rank)
+    segs      the ranks' global positions
+    returns   P fp32 tensors [B, Hb, L_t, d], rows in rank t's storage order
+    """
+    B, Hb, S, d = partials[0].shape
+    if _global_length(segs) != S:
+        raise ValueError("the segments must tile the partials' sequence")
+    outs = []
+    for sg in segs:
+        L = sum(n for _, n in sg)
+        y = torch.empty((B, Hb, L, d), dtype=torch.float32, device=partials[0].device)
+        off = 0
+        for start, n in sg:
+            _lib.ra_copy_rows(partials[0], start, y, off, n, stream=stream)
+            for p in partials[1:]:
+                _lib.ra_add_rows(p, start, y, off, n, stream=stream)
+            off += n
+        outs.append(y)
+    return outs
 
 
 def heads_to_group(blocks: Sequence[torch.Tensor], segs: Sequence[Segs], g: int, P: int, stream=None):

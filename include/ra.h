@@ -277,9 +277,13 @@ ra_status ra_factored_spatial(const void* q, const void* k, const void* v, ra_dt
 /*
  * ra_factored_temporal — temporal half of factored video attention (same
  * section): each query at (t, s) attends without a mask to the T keys
- * {t'*S_sp + s : t' < T} at its spatial position. T must be 1..16.
+ * {t'*S_sp + s : t' < T} at its spatial position. T must be 1..128 (the
+ * page's clips run to 48 and 120 frames, "What the numbers look like"); up
+ * to 16 frames one wave serves a spatial position, longer clips one
+ * workgroup with the position's K and V frames staged in LDS.
  * Arguments and errors as ra_factored_spatial (without the per-frame size
- * limit); T > 16 is RA_ERR_UNSUPPORTED.
+ * limit); T > 128 is RA_ERR_UNSUPPORTED, and so is T > 16 when one (batch,
+ * head) slice, T * S_sp * d elements, exceeds 2^31 - 1 bytes.
  */
 ra_status ra_factored_temporal(const void* q, const void* k, const void* v, ra_dtype dt,
                                int32_t B, int32_t H, int32_t T, int32_t S_sp, int32_t d,
@@ -316,6 +320,25 @@ ra_status ra_kv_pass(const void* k_src, const void* v_src, void* k_dst, void* v_
 ra_status ra_copy_rows(const void* src, int64_t src_slice_rows, int64_t src_row0,
                        void* dst, int64_t dst_slice_rows, int64_t dst_row0,
                        int64_t nslices, int64_t nrows, int64_t row_bytes, hipStream_t stream);
+
+/*
+ * ra_add_rows — the reduce-scatter that the Ultralytics glossary lists next to
+ * all-gather ("How Context Parallelism Works"), in the form the backward pass
+ * of the all-gather variant needs: every rank's gradient of the gathered K/V
+ * covers all positions, and the rows a rank owns must be summed over the
+ * ranks. One GPU simulates the exchange; this call is its arithmetic:
+ *   dst[s][dst_row0 + i][c] += src[s][src_row0 + i][c]
+ * for s < nslices, i < nrows, c < d, fp32, with slice s of src starting at
+ * src + s * src_slice_rows * d floats (likewise dst). Device pointers, 16-byte
+ * aligned; d a multiple of 4. Asynchronous on `stream`.
+ * Errors: RA_ERR_INVALID_ARG for null pointers, nslices <= 0, nrows < 0,
+ *   d <= 0 or not a multiple of 4, a row range outside its slice, misaligned
+ *   pointers, or source and destination ranges that overlap. nrows == 0 is a
+ *   no-op.
+ */
+ra_status ra_add_rows(const float* src, int64_t src_slice_rows, int64_t src_row0,
+                      float* dst, int64_t dst_slice_rows, int64_t dst_row0,
+                      int64_t nslices, int64_t nrows, int32_t d, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* ra_status_string(ra_status s);

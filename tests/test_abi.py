@@ -118,7 +118,11 @@ def test_factored_validation(lib):
         assert fn(ptr(0), ptr(1), ptr(2), 1, 1, 1, 4, 9, 128, 0.1, ptr(1), None, None) == INV
         assert fn(ptr(0), ptr(1), ptr(2), 0, 1, 1, 4, 9, 128, 0.1, ptr(3), None, None) == UNS
         assert fn(ptr(0), ptr(1), ptr(2), 1, 1, 1, 4, 9, 32, 0.1, ptr(3), None, None) == UNS
-    assert lib.ra_factored_temporal(ptr(0), ptr(1), ptr(2), 1, 1, 1, 17, 9, 128, 0.1, ptr(3),
+    # a long clip's slice must be addressable with 32-bit byte offsets
+    assert lib.ra_factored_temporal(ptr(0), ptr(1), ptr(2), 1, 1, 1, 120, 1 << 17, 128, 0.1, ptr(3),
+                                    None, None) == UNS
+    # clips longer than 128 frames are not supported (the pages' longest is 120)
+    assert lib.ra_factored_temporal(ptr(0), ptr(1), ptr(2), 1, 1, 1, 129, 9, 128, 0.1, ptr(3),
                                     None, None) == UNS
     # offsets inside one frame of the spatial kernel are 32-bit
     assert lib.ra_factored_spatial(ptr(0), ptr(1), ptr(2), 1, 1, 1, 1, 1 << 23, 128, 0.1, ptr(3),
@@ -262,6 +266,19 @@ def test_copy_rows_validation(lib):
     assert c(ptr(0), 64, 0, ptr(1), 64, 60, 4, 8, 256, None) == INV         # past the destination slice
     assert c(ptr(0), 64, -1, ptr(1), 64, 0, 4, 8, 256, None) == INV
     assert c(ptr(0), 64, 0, ptr(0) + 256 * 8, 64, 0, 4, 8, 256, None) == INV  # overlapping ranges
+
+
+def test_add_rows_validation(lib):
+    a = lib.ra_add_rows
+    assert a(ptr(0), 64, 0, ptr(1), 64, 0, 4, 0, 128, None) == _lib.RA_OK  # no rows: no-op
+    assert a(None, 64, 0, ptr(1), 64, 0, 4, 8, 128, None) == INV
+    assert a(ptr(0), 64, 0, ptr(1), 64, 0, 0, 8, 128, None) == INV          # no slices
+    assert a(ptr(0), 64, 0, ptr(1), 64, 0, 4, 8, 126, None) == INV          # d not a multiple of 4
+    assert a(ptr(0), 64, 60, ptr(1), 64, 0, 4, 8, 128, None) == INV         # past the source slice
+    assert a(ptr(0), 64, 0, ptr(1), 64, 60, 4, 8, 128, None) == INV         # past the destination slice
+    assert a(ptr(0), 64, -1, ptr(1), 64, 0, 4, 8, 128, None) == INV
+    assert a(ptr(0) + 4, 64, 0, ptr(1), 64, 0, 4, 8, 128, None) == INV      # misaligned
+    assert a(ptr(0), 64, 0, ptr(0) + 512 * 8, 64, 0, 4, 8, 128, None) == INV  # overlapping ranges
 
 
 def test_variants_refuse_segments_that_do_not_tile_the_sequence():

@@ -854,6 +854,59 @@ def test_allgather_every_rank(gpu_lib, wname):
                      f"all-gather {w.name} r{rank}")
 
 
+def test_add_rows_is_an_fp32_add(gpu_lib):
+    banner("ra_add_rows: strided row accumulate over slices, bitwise against an fp32 add")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    src = torch.randn((2, 3, 300, 128), generator=g, device="cuda")
+    dst = torch.randn((2, 3, 100, 128), generator=g, device="cuda")
+    ref = dst.clone()
+    ref[:, 1:3, 7:7 + 61] += src[:, 0:2, 200:200 + 61].clone()
+    # slices 1..2 of every batch of dst: slices are the flattened leading dims
+    for b in range(2):
+        _lib.ra_add_rows(src, 200, dst, 7, 61, src_slice0=3 * b, dst_slice0=3 * b + 1, nslices=2)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, ref)
+
+
+@pytest.mark.parametrize("wname", ["causal-bf16-4k-cp2", "causal-bf16-4k-cp2-gqa4"])
+def test_allgather_backward_reduce_scatter(gpu_lib, wname):
+    # backward of the all-gather variant: every rank's dK/dV of the gathered
+    # K/V, reduce-scattered to the owning ranks, equals the gradient of
+    # full-sequence attention at each rank's positions (the ranks' queries
+    # together are the whole sequence)
+    w = configs.RING_WORKLOADS[wname]
+    banner(f"all-gather backward + reduce-scatter, {w.name}, all ranks")
+    cases = [RingCase(w, r) for r in range(w.P)]
+    dqs, pk, pv = [], [], []
+    for r, case in enumerate(cases):
+        out, lse = variants.run_allgather(case.q, case.q_segs, case.kv, case.kv_segs, w.causal, scale=w.scale)
+        do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, ringcase_positions(w, r), w.d, w.dtype, "cuda")
+        dq, dk, dv = variants.allgather_bwd(case.q, case.q_segs, case.kv, case.kv_segs, w.causal, out, lse, do,
+                                            scale=w.scale)
+        dqs.append(dq)
+        pk.append(dk)
+        pv.append(dv)
+    segs = cases[0].kv_segs
+    dks = variants.reduce_scatter(pk, segs)
+    dvs = variants.reduce_scatter(pv, segs)
+    torch.cuda.synchronize()
+    allpos = np.arange(w.S)
+    G = w.H // w.Hkv
+    for b in range(w.B):
+        ex = lambda tid, h: seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, tid, b, h, allpos, w.d),
+                                                             w.dtype))
+        q = np.stack([ex(seeded.Q, h) for h in range(w.H)])
+        do = np.stack([ex(DOUT, h) for h in range(w.H)])
+        k = np.stack([ex(seeded.K, h) for h in range(w.Hkv)])
+        v = np.stack([ex(seeded.V, h) for h in range(w.Hkv)])
+        rq, rk, rv = oracle.grouped_attention_grads(q, allpos, k, v, allpos, w.scale, w.causal, do)
+        for r in range(w.P):
+            pos = ringcase_positions(w, r)
+            grad_close(dqs[r][b].cpu().double().numpy(), rq[:, pos], f"dq rank {r} (G={G})")
+            grad_close(dks[r][b].cpu().double().numpy(), rk[:, pos], f"dk rank {r} after reduce-scatter")
+            grad_close(dvs[r][b].cpu().double().numpy(), rv[:, pos], f"dv rank {r} after reduce-scatter")
+
+
 @pytest.mark.parametrize("wname", ["causal-bf16-4k-cp2", "causal-bf16-4k-cp2-gqa4"])
 def test_head_all_to_all_every_group(gpu_lib, wname):
     w = configs.RING_WORKLOADS[wname]
