@@ -36,7 +36,9 @@
 //   feeds the matrix core while the other computes exponentials.
 // * The running maximum only moves when a tile's maximum exceeds it by more
 //   than 2^8 in weight (lazy rescale); the state stays exact because O and l
-//   are always expressed relative to the same reference value m.
+//   are always expressed relative to the same reference value m. The tile's
+//   row maxima are only formed when a lane's share of the tile sum shows that
+//   such a move may be due.
 // * Tiles whose keys all lie after the last query (causal) are never loaded;
 //   tiles straddling the diagonal, and ragged tails, are masked per element.
 // * Each of the 8 XCDs owns a contiguous range of items (whole slices), so a
@@ -59,6 +61,11 @@ constexpr int kBQ = 32 * kWaves;        // query rows per work item
 constexpr int kNST = kBK / 32;          // 32-key halves per tile
 constexpr int kRun = 1088;              // LDS bytes per 1 KiB load run, padded
 constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+// A weight above 2^kTau (a tile maximum more than kTau above the reference,
+// when the rescale rule moves it) makes its lane's share of the tile sum
+// exceed 2^kTau; while every lane's share stays within it, no rescale is due
+// and the row maximum is not needed.
+constexpr float kSumMax = 256.0f;       // 2^kTau
 constexpr int kXcds = 8;
 
 template <int D>
@@ -443,6 +450,10 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
       // compare the lane-independent part of e with a per-lane limit, so that
       // the 32 offsets are immediates rather than registers
       const int32_t limh = lim - 4 * h;
+      // in place (each select is tied to its score register), so that the
+      // masked and unmasked paths leave the scores in the same registers and
+      // the unmasked path needs no copies
+      const float ninf = kNegInf;
 #pragma unroll
       for (int st = 0; st < kNST; ++st)
 #pragma unroll
@@ -450,7 +461,10 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int e = 32 * st + 8 * i + j;  // + 4h
-            sc[st][4 * i + j] = e > limh ? kNegInf : sc[st][4 * i + j];
+            asm volatile("v_cmp_lt_i32 vcc, %2, %3\n\tv_cndmask_b32 %0, %0, %1, vcc"
+                         : "+v"(sc[st][4 * i + j])
+                         : "v"(ninf), "v"(limh), "n"(e)
+                         : "vcc");
           }
     } else {
       // only the tile holding the segment boundary straddles it; an opaque
@@ -507,18 +521,24 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     }
   };
 
-  // exponentials of one tile into bf16 B operands (and the row-sum shares,
-  // summed in fp32 before rounding so that lse keeps full precision)
-  auto exps = [&]() RA_INLINE {
+  // exponentials of one tile against the current reference, into bf16 B
+  // operands; tsum gets this lane's share of the tile's row sum (in fp32,
+  // before the rounding, so that lse keeps full precision)
+  auto exps = [&](float& tsum) RA_INLINE {
     const float mus = mu == kNegInf ? 0.f : mu;
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int st = 0; st < kNST; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = fast_exp2(__builtin_fmaf(sc[st][r], c_log2, -mus));
-        lpart[r & 1] += pr;
+        if (r & 1)
+          s1 += pr;
+        else
+          s0 += pr;
         pf[2 * st + r / 8][r % 8] = to_bf16(pr);
       }
+    tsum = s0 + s1;
   };
 
   // The matrix phase of one tile in a fixed order: the score MFMAs of the next
@@ -557,12 +577,23 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     }
   };
 
-  // softmax of stream tile m of the current item (scores in sc)
+  // softmax of stream tile m of the current item (scores in sc). The weights
+  // are taken against the current reference first: the row maxima are only
+  // formed, and the rescale rule applied, when some lane's share of the tile
+  // sum exceeds kSumMax (or is not finite), or a row that had no visible key
+  // yet meets one; then the weights are taken again. The row maximum is a
+  // fifth of the vector work, and this way it is skipped on almost every tile.
   auto vector_phase = [&](int32_t m) RA_INLINE {
     const TileInfo ti = tile_info(m);
     if (ti.mask) apply_mask(ti);
-    rescale(rowmax());
-    exps();
+    float tsum;
+    exps(tsum);
+    const bool check = !(tsum <= kSumMax) || (mu == kNegInf && tsum > 0.f);
+    if (__builtin_amdgcn_ballot_w64(check)) {
+      rescale(rowmax());
+      exps(tsum);
+    }
+    lpart[0] += tsum;
     // the weights are complete here: without this use the compiler sinks part
     // of the exponentials and conversions past the barrier into the other
     // phase, where the same wave then issues them between its products
