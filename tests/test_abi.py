@@ -19,10 +19,13 @@ HEADER = os.path.join(ROOT, "include", "ra.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(_lib.LIB_PATH):
+    # RA_TEST_ABI_LIB: the host-only build of the ABI layer with
+    # AddressSanitizer and counting launcher stand-ins (tests/test_abi_asan.py)
+    path = os.environ.get("RA_TEST_ABI_LIB", _lib.LIB_PATH)
+    if not os.path.exists(path):
         from context_attention_ra_amd import build
         build.build()
-    return _lib.load()
+    return _lib.load(path)
 
 
 def declared_functions():
@@ -374,3 +377,24 @@ def test_binding_checks_dtypes_and_devices_before_any_library_call(monkeypatch):
         _lib.ra_kv_pass(q, q, torch.empty_like(q), torch.empty_like(q))
     with pytest.raises(ValueError, match="GPU"):
         _lib.ra_copy_rows(q, 0, torch.empty_like(q), 0, 8)
+
+
+def test_rejected_calls_launch_nothing(lib):
+    # only the host build with counting launcher stand-ins can see launches
+    if not hasattr(lib, "ra_test_launch_count"):
+        pytest.skip("needs the host build of the ABI layer with counting launchers")
+    count = lib.ra_test_launch_count
+    count.restype = ctypes.c_int32
+    before = count()
+    for kw in (dict(q=0), dict(scale=float("nan")), dict(qs=((0, 63),)), dict(o=ptr(0)), dict(d=96)):
+        assert step(lib, **kw) != _lib.RA_OK
+    for kw in (dict(dout=0), dict(flags=4 | 8), dict(dk=ptr(1)), dict(d=96)):
+        assert step_bwd(lib, **kw) != _lib.RA_OK
+    assert lib.ra_factored_temporal(ptr(0), ptr(1), ptr(2), 1, 1, 1, 129, 9, 128, 0.1, ptr(3), None,
+                                    None) != _lib.RA_OK
+    assert lib.ra_add_rows(ptr(0), 64, 60, ptr(1), 64, 0, 4, 8, 128, None) != _lib.RA_OK
+    assert count() == before
+    # and valid calls do reach their launchers
+    assert step(lib) == _lib.RA_OK
+    assert lib.ra_add_rows(ptr(0), 64, 0, ptr(1), 64, 0, 4, 8, 128, None) == _lib.RA_OK
+    assert count() == before + 2
