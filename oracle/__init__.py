@@ -24,6 +24,7 @@ Sources (cited by page title and section):
 
 from .attention import (  # noqa: F401
     attention_grads,
+    attention_kv_grads_rows,
     attention_rows,
     factored_spatial,
     factored_temporal,

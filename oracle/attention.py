@@ -112,6 +112,45 @@ def attention_grads(q, q_pos, k, v, k_pos, scale, causal, do):
     return dq, dk, dv
 
 
+def attention_kv_grads_rows(q, q_pos, k, v, k_pos, scale, causal, do, key_rows, fwd=None):
+    """dk and dv of selected key rows, for sequences too long for the full
+    probability matrix of ``attention_grads``.
+
+    The same derivative (k8ai "Communication profile": the ring also runs
+    backward): with lse_i and o_i of every query row from ``attention_rows``
+    and delta_i = <do_i, o_i>, for each selected key j
+        P_ij  = exp(s_ij - lse_i) (0 if j is not visible to i)
+        dv_j  = sum_i P_ij do_i
+        dk_j  = scale * sum_i P_ij (<do_i, v_j> - delta_i) q_i
+    Only the selected columns of P are formed.
+
+    key_rows: indices into k, v, k_pos; other arguments as ``attention_grads``.
+    fwd: optional (o, lse) of these query rows from ``attention_rows`` (a long
+    forward can then be computed in pieces by the caller)
+    returns (dk (m, d), dv (m, d)) in fp64
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    key_rows = np.asarray(key_rows, dtype=np.int64)
+    o, lse = attention_rows(q, q_pos, k, v, k_pos, scale, causal) if fwd is None else fwd
+    delta = np.sum(do * o, axis=1)
+    kj, vj, pj = k[key_rows], v[key_rows], k_pos[key_rows]
+    s = float(scale) * (q @ kj.T)
+    visible = np.ones_like(s, dtype=bool)
+    if causal:
+        visible = pj[None, :] <= q_pos[:, None]
+    has_key = np.isfinite(lse)
+    lse_safe = np.where(has_key, lse, 0.0)
+    P = np.where(visible & has_key[:, None], np.exp(np.where(visible, s, 0.0) - lse_safe[:, None]), 0.0)
+    dP = do @ vj.T
+    ds = P * (dP - delta[:, None])
+    return float(scale) * (ds.T @ q), P.T @ do
+
+
 def grouped_attention(q, q_pos, k, v, k_pos, scale, causal):
     """Attention of H query heads when groups of query heads share a K/V head.
 

@@ -739,6 +739,46 @@ def test_bwd_video_dit_432k_sampled_dq(gpu_lib):
         assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
 
 
+@pytest.mark.slow
+def test_bwd_video_dit_432k_sampled_dkdv(gpu_lib):
+    # dK/dV at the video share: rank 3's contributions to every block, on
+    # sampled key rows of head 7 (each needs the lse and output of all 54,000
+    # local queries against the 432,000 keys: about 1.2e13 fp64 FLOP, computed
+    # in pieces with progress lines)
+    w = configs.VIDEO_DIT_CP8
+    rank, h = 3, 7
+    banner(f"backward ring, {w.name} rank {rank}: dk, dv of sampled key rows of head {h}")
+    case = RingCase(w, rank)
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, rank, w.causal, scale=w.scale)
+    qpos = ringcase_positions(w, rank)
+    do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, qpos, w.d, w.dtype, "cuda")
+    _, dkv = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, rank, w.causal, out, lse, do,
+                          scale=w.scale)
+    torch.cuda.synchronize()
+    for dk, dv in dkv:
+        assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    allpos = np.arange(w.S)
+    ex = lambda tid, r: seeded.exact_f64(seeded.to_dtype(seeded.normal_rows_at(w.wid, tid, 0, h, r, w.d), w.dtype))
+    qf, kf, vf, dof = ex(seeded.Q, qpos), ex(seeded.K, allpos), ex(seeded.V, allpos), ex(DOUT, qpos)
+    n = qf.shape[0]
+    o, lse_ref = np.zeros((n, w.d)), np.zeros(n)
+    step = 6000
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        o[r0:r1], lse_ref[r0:r1] = oracle.attention_rows(qf[r0:r1], qpos[r0:r1], kf, vf, allpos, w.scale, False)
+        print(f"  oracle forward rows {r1}/{n}", flush=True)
+    # per block: its first and last local row and 30 more, uniform from a seed
+    rng = np.random.default_rng([77, rank, h])
+    for t in range(w.P):
+        kpos = ringcase_positions(w, t)
+        local = np.unique(np.concatenate([[0, kpos.size - 1], rng.choice(kpos.size, 30, replace=False)]))
+        rk, rv = oracle.attention_kv_grads_rows(qf, qpos, kf, vf, allpos, w.scale, False, dof, kpos[local],
+                                                fwd=(o, lse_ref))
+        idx = torch.as_tensor(local, device=dkv[t][0].device)
+        grad_close(dkv[t][0][0, h].index_select(0, idx).cpu().double().numpy(), rk, f"dk block {t}, {local.size} rows")
+        grad_close(dkv[t][1][0, h].index_select(0, idx).cpu().double().numpy(), rv, f"dv block {t}, {local.size} rows")
+
+
 def test_bwd_llm_32k_rank0_dkdv_two_heads(gpu_lib):
     # dK/dV of every block at the full share: rank 0's contributions, all key
     # rows of heads 0 and H-1 (the oracle's full gradient costs about 10 s per head)

@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attention_grads, attention_rows, factored_spatial, factored_temporal,
-                    grouped_attention, grouped_attention_grads, merge_lse)
+from oracle import (attention_grads, attention_kv_grads_rows, attention_rows, factored_spatial,
+                    factored_temporal, grouped_attention, grouped_attention_grads, merge_lse)
 
 
 def brute_attention(q, q_pos, k, v, k_pos, scale, causal):
@@ -210,6 +210,41 @@ def test_grads_match_torch_autograd_float64(causal):
     out.backward(torch.from_numpy(do)[None, None])
     for mine, ref in ((dq, tq), (dk, tk), (dv, tv)):
         np.testing.assert_allclose(mine, ref.grad[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kv_grads_of_selected_rows(causal):
+    # the selected-rows form against numerical derivatives of the forward
+    # definition (for the chosen key rows) and against PyTorch autograd
+    n, S, d = 5, 9, 3
+    q, k, v, do = rnd(70, n, d), rnd(71, S, d), rnd(72, S, d), rnd(73, n, d)
+    qp, kp = np.array([0, 2, 5, 7, 8]), np.random.default_rng(74).permutation(S)
+    rows = np.array([7, 0, 4])
+    scale = 0.7
+    dk, dv = attention_kv_grads_rows(q, qp, k, v, kp, scale, causal, do, rows)
+    eps = 1e-6
+    for name, x, g in (("k", k, dk), ("v", v, dv)):
+        num = np.zeros((rows.size, d))
+        for a, r in enumerate(rows):
+            for c in range(d):
+                xp, xm = x.copy(), x.copy()
+                xp[r, c] += eps
+                xm[r, c] -= eps
+                args = {"k": k, "v": v}
+                lp = _loss(q=q, **{**args, name: xp}, qp=qp, kp=kp, scale=scale, causal=causal, do=do)
+                lm = _loss(q=q, **{**args, name: xm}, qp=qp, kp=kp, scale=scale, causal=causal, do=do)
+                num[a, c] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)
+    L = 40
+    q, k, v, do = rnd(75, L, 8), rnd(76, L, 8), rnd(77, L, 8), rnd(78, L, 8)
+    pos = np.arange(L)
+    rows = np.array([0, 13, 39, 21])
+    dk, dv = attention_kv_grads_rows(q, pos, k, v, pos, 8 ** -0.5, causal, do, rows)
+    tq, tk, tv = (torch.from_numpy(a)[None, None].requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    out.backward(torch.from_numpy(do)[None, None])
+    np.testing.assert_allclose(dk, tk.grad[0, 0].numpy()[rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad[0, 0].numpy()[rows], rtol=1e-10, atol=1e-12)
 
 
 def test_grads_invariants():
