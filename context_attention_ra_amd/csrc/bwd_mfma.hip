@@ -18,6 +18,13 @@
 //   in registers), dS^T formed in registers (every lane owns one query, so
 //   lse and delta are lane scalars), dQ^T += K^T dS^T with the transposing
 //   LDS read for K^T and dS^T as the B operand straight from the registers.
+//   Eight waves (256 queries) share a 4-deep LDS ring of K/V tiles; as in the
+//   forward ring step, the two halves of the workgroup (one wave of each on
+//   every SIMD) run the same per-tile program one phase apart, so one wave
+//   of a SIMD issues the products (dQ of tile n, S and dP of tile n+1) while
+//   the other forms the weights of its next tile. Without that offset the
+//   barrier of every tile keeps both waves of a SIMD in the same phase, and
+//   products and exponentials take turns instead of overlapping.
 // * bwd_dkdv: each wave owns 32 key rows and streams 64-row Q/dO tiles:
 //   S = Q K^T and dP = dO V^T (every lane owns one key; the per-row lse and
 //   delta of the tile come from LDS), then dV^T += dO^T P and dK^T += Q^T dS.
@@ -39,29 +46,46 @@
 namespace ra {
 namespace {
 
-constexpr int kBW = 4;                // waves per workgroup of the dQ kernel
-constexpr int kBThreads = 64 * kBW;
-constexpr int kOwn = 32 * kBW;        // owned rows per workgroup of the dQ kernel
+constexpr int kQW = 8;                // waves per workgroup of the dQ kernel
+constexpr int kQThreads = 64 * kQW;
+constexpr int kQOwn = 32 * kQW;       // owned query rows per workgroup of the dQ kernel
+constexpr int kQStages = 4;           // LDS ring depth of the dQ kernel
+constexpr int kQAhead = 3;            // LDS operands read ahead of their MFMA (dQ kernel)
 constexpr int kKW = 8;                // waves per workgroup of the dK/dV kernel
 constexpr int kKThreads = 64 * kKW;
 constexpr int kKOwn = 32 * kKW;       // owned keys per workgroup of the dK/dV kernel
 using namespace tiles;
-static_assert(BLay<128>::NRUN % kBW == 0 && BLay<128>::NRUN % kKW == 0 && BLay<64>::NRUN % kKW == 0,
+static_assert(BLay<128>::NRUN % kKW == 0 && BLay<64>::NRUN % kKW == 0 && kQW == kKW,
               "load runs must split evenly over the waves");
 
+// s_waitcnt encodings (gfx9): wait until at most n vector-memory ops are pending
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// The dQ kernel body is written as lambdas; with two copies of its schedule
+// the inliner would otherwise turn some of them into calls with stack frames.
+#define RA_BINLINE __attribute__((always_inline))
+
+template <bool B>
+struct GroupC {
+  static constexpr bool value = B;
+};
 
 // ---------------------------------------------------------------------------
-// dQ: owned queries, streamed K/V tiles
+// dQ: owned queries, streamed K/V tiles, two wave groups in ping-pong
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
     int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, float scale,
     int32_t init, float* __restrict__ dQ, int32_t nqt, int32_t per_xcd, int32_t group) {
   using L = BLay<D>;
   constexpr int KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  constexpr int TB = 2 * L::TBYTES;          // K tile, then V tile
+  constexpr int NDMA = 2 * (L::NRUN / kQW);  // load instructions per wave per tile
+  __shared__ __attribute__((aligned(16))) char smem[kQStages * TB];
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the group branch is scalar
   const int32_t logical = xcd_logical(per_xcd);
   if (logical >= nb * nqt) return;
   const int32_t prob = logical / nqt;
@@ -69,7 +93,7 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
   // dispatched first and the light ones fill the tail (the workgroups of an
   // XCD start in logical order as CUs free up)
   const int32_t qt = logical - prob * nqt;
-  const int32_t q0 = (CAUSAL ? nqt - 1 - qt : qt) * kOwn;
+  const int32_t q0 = (CAUSAL ? nqt - 1 - qt : qt) * kQOwn;
 
   const int32_t w_r0 = q0 + 32 * w;
   const int32_t qrow = w_r0 + l32;
@@ -84,7 +108,7 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
   TileRuns tr{0, 0, 0, 0};
   if (CAUSAL) {
     int32_t lo, hi;
-    seg_range(qs, q0, min(q0 + kOwn, Lq), lo, hi);
+    seg_range(qs, q0, min(q0 + kQOwn, Lq), lo, hi);
     tr = tiles_from(ks, Lk, 0, hi, false);
   } else {
     tr.n0 = tr.n = (Lk + kT - 1) / kT;
@@ -100,17 +124,7 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     }
     return;
   }
-
-  const size_t kvbase = (size_t)(prob / group) * Lk * D;  // the K/V head of this query head
-  const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + kvbase, Lk, D);
-  const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + kvbase, Lk, D);
-  auto fetch = [&](int32_t n) {
-    char* st = smem + (n & 1) * L::STAGE;
-    const int32_t r0 = tile_row0(tr, n);
-    load_tile<D, kBW>(krs, st, r0, w, lane);
-    load_tile<D, kBW>(vrs, st + L::TBYTES, r0, w, lane);
-  };
-  fetch(0);
+  const int32_t nt = tr.n;
 
   // this lane's query and upstream-gradient rows (B operands), lse and delta
   bf16x8 qf[KS], df[KS];
@@ -126,20 +140,52 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
   const float lse2 = (qvalid && lse != kNegInf) ? lse * kLog2e : __builtin_inff();
   const float dlt = Dlt[rbase + qrow_c];
 
+  const size_t kvbase = (size_t)(prob / group) * Lk * D;  // the K/V head of this query head
+  const __amdgpu_buffer_rsrc_t krs = slice_rsrc(K + kvbase, Lk, D);
+  const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(V + kvbase, Lk, D);
+  int32_t fg = 0;  // next tile to request; tile n sits in stage n % kQStages
+  auto fetch_next = [&]() RA_BINLINE {
+    char* st = smem + (fg % kQStages) * TB;
+    const int32_t r0 = __builtin_amdgcn_readfirstlane(tile_row0(tr, fg));
+    load_tile<D, kQW>(krs, st, r0, w, lane);
+    load_tile<D, kQW>(vrs, st + L::TBYTES, r0, w, lane);
+    ++fg;
+  };
+#pragma unroll
+  for (int i = 0; i < kQStages; ++i)
+    if (i < nt) fetch_next();
+
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
+  f32x16 s[2], dpv[2];  // S^T, dP^T of the tile whose weights come next
+  bf16x8 dsb[4];        // dS^T of the tile whose dQ products come next (16-key slices)
   const int trb = tr_base<D>(lane);
 
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  __syncthreads();
-  for (int32_t n = 0; n < tr.n; ++n) {
-    if (n + 1 < tr.n) fetch(n + 1);
-    const char* kt = smem + (n & 1) * L::STAGE;
-    const char* vt = kt + L::TBYTES;
+  // step i of S^T = K Q^T and dP^T = V dO^T (k-step i/4, 32-key half (i/2)%2,
+  // K or V): its A operand from the tile at kt, and its product
+  auto m1_operand = [&](const char* kt, int i) RA_BINLINE -> bf16x8 {
+    const int ksi = i / 4, st = (i / 2) % 2, tens = i % 2;
+    return row_operand<D>(kt + tens * L::TBYTES, st, ksi, l32, h);
+  };
+  auto m1_step = [&](int i, const bf16x8& op) RA_BINLINE {
+    const int ksi = i / 4, st = (i / 2) % 2, tens = i % 2;
+    if (tens == 0)
+      s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qf[ksi], s[st], 0, 0, 0);
+    else
+      dpv[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, df[ksi], dpv[st], 0, 0, 0);
+  };
+  // S^T and dP^T of tile n alone (the first tile of each group)
+  auto scores = [&](int32_t n) RA_BINLINE {
+    const char* kt = smem + (n % kQStages) * TB;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) s[st] = dpv[st] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 4 * KS; ++i) m1_step(i, m1_operand(kt, i));
+  };
+  // weights of tile n: P = exp(S - lse) on visible pairs, dS = P (dP - delta)
+  auto vector_phase = [&](int32_t n) RA_BINLINE {
     const int32_t kt0 = tile_row0(tr, n);
-    // element mask: the ragged tail of the block, and (causal) keys after
-    // some query of this wave
     bool need_mask = kt0 + kT > Lk;
     if (CAUSAL) {
       int32_t klo, khi;
@@ -147,21 +193,6 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
       (void)klo;
       need_mask = need_mask || khi > w_qlo;
     }
-    // the products of both 32-key halves first, so that the second half's
-    // run on the matrix core while the first half's weights are formed
-    f32x16 s[2], dpv[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = f32x16{};
-      dpv[st] = f32x16{};
-#pragma unroll
-      for (int ksi = 0; ksi < KS; ++ksi) {
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(kt, st, ksi, l32, h), qf[ksi], s[st], 0, 0, 0);
-        dpv[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vt, st, ksi, l32, h), df[ksi], dpv[st], 0, 0, 0);
-      }
-    }
-    // masked scores become -inf (weight exactly 0) in one block per tile, so
-    // that the exponentials below are straight-line code
     if (need_mask) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -177,21 +208,100 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
       f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        // c_log2 > 0 and lse2 is finite or +inf, so a -inf score gives p = 0
         const float p = fast_exp2(__builtin_fmaf(s[st][r], c_log2, -lse2));
         ds[r] = p * (dpv[st][r] - dlt);
       }
-      bf16x8 b0, b1;
-      pack_b(ds, b0, b1);
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, trb, 2 * st, t), b0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, trb, 2 * st + 1, t), b1, acc[t], 0, 0, 0);
-      }
+      pack_b(ds, dsb[2 * st], dsb[2 * st + 1]);
     }
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-  }
+    // the weights are complete here: without this use the compiler sinks part
+    // of the exponentials into the next phase, between the same wave's products
+    asm volatile("" ::"v"(dsb[0]), "v"(dsb[1]), "v"(dsb[2]), "v"(dsb[3]));
+  };
+  // matrix phase n: S^T, dP^T of tile n+1, then dQ^T += K^T dS^T of tile n;
+  // every LDS operand is read kQAhead steps before its MFMA, and scheduling
+  // barriers keep that order
+  auto matrix = [&](int32_t n) RA_BINLINE {
+    __builtin_amdgcn_s_setprio(1);
+    // past the last tile the S^T, dP^T products read a stage that holds no
+    // tile of this workgroup; their results are never used
+    const char* kn = smem + ((n + 1) % kQStages) * TB;
+    const char* kc = smem + (n % kQStages) * TB;
+    constexpr int N1 = 4 * KS, N2 = 4 * DT;
+    auto operand = [&](int i) RA_BINLINE -> bf16x8 {
+      if (i < N1) return m1_operand(kn, i);
+      const int j = i - N1;
+      return tr_operand<D>(kc, trb, j / DT, j % DT);
+    };
+#pragma unroll
+    for (int st = 0; st < 2; ++st) s[st] = dpv[st] = f32x16{};
+    bf16x8 op[kQAhead];
+#pragma unroll
+    for (int j = 0; j < kQAhead; ++j) op[j] = operand(j);
+#pragma unroll
+    for (int i = 0; i < N1 + N2; ++i) {
+      const bf16x8 cur = op[i % kQAhead];
+      if (i < N1) {
+        m1_step(i, cur);
+      } else {
+        const int j = i - N1, t = j % DT;
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, dsb[j / DT], acc[t], 0, 0, 0);
+      }
+      if (i + kQAhead < N1 + N2) op[i % kQAhead] = operand(i + kQAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Ping-pong as in the forward ring step: waves 0..3 (group A) and 4..7
+  // (group B, one of each on every SIMD) run the same per-tile program one
+  // slot apart, so one wave of a SIMD issues products while the other forms
+  // weights. Group A: slot 0 = scores and weights of tile 0, slot 2n+1 =
+  // matrix phase n, slot 2n+2 = weights of tile n+1; group B one slot later.
+  // Tile n is read from matrix phase n-1 to matrix phase n of group B (slot
+  // 2n+2); at the start of slot 2n+3 tile n+4 is requested into its stage.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  auto run = [&](auto grp) RA_BINLINE {
+    constexpr bool late = decltype(grp)::value;
+    // end of slot 2n: tile n+1 must be in LDS; tiles requested after it may
+    // stay in flight
+    auto slot_end = [&](int32_t n) RA_BINLINE {
+      const int32_t in_flight = fg - (n + 2);
+      if (in_flight >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NDMA));
+      else if (in_flight == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+    };
+    if (!late) {
+      scores(0);
+      vector_phase(0);
+    }
+    slot_end(0);
+    for (int32_t n = 0; n < nt; ++n) {
+      if (fg == n + kQStages - 1 && fg < nt) fetch_next();
+      if (!late) {
+        matrix(n);
+      } else {
+        if (n == 0) scores(0);
+        vector_phase(n);
+      }
+      __syncthreads();
+      if (!late) {
+        if (n + 1 < nt) vector_phase(n + 1);
+      } else {
+        matrix(n);
+      }
+      slot_end(n + 1);
+    }
+  };
+  if (w >= kQW / 2)
+    run(GroupC<true>{});
+  else
+    run(GroupC<false>{});
+
   if (!qvalid) return;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
@@ -420,12 +530,12 @@ DevSegs bdev(const HostSegs& s) { return DevSegs{s.start0, s.start1, s.len0, s.l
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
-  const int32_t nqt = (a.Lq + kOwn - 1) / kOwn, nkt = (a.Lk + kKOwn - 1) / kKOwn;
+  const int32_t nqt = (a.Lq + kQOwn - 1) / kQOwn, nkt = (a.Lk + kKOwn - 1) / kKOwn;
   const int32_t nkv = a.nb / a.group;
   const int32_t pq = (int32_t)(((int64_t)a.nb * nqt + kXcdsB - 1) / kXcdsB);
   const int32_t pk = (int32_t)(((int64_t)nkv * nkt + kXcdsB - 1) / kXcdsB);
   if (a.run_dq) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(kXcdsB * pq), dim3(kBThreads), 0, st,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(kXcdsB * pq), dim3(kQThreads), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.dout,
                        a.lse, a.delta, a.nb, a.Lq, a.Lk, bdev(a.qs), bdev(a.ks), c, a.scale,
                        (int32_t)a.init_dq, a.dq, nqt, pq, a.group);
