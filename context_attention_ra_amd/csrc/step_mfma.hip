@@ -361,21 +361,32 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   };
   auto end_item = [&]() RA_INLINE {
     const float lsum = partner32_sum(lpart[0] + lpart[1]);
-    if (!wave_active || !qvalid) return;
+    if (!wave_active) return;
     const size_t r = (size_t)cc.it.prob * Lq + qrow;
     if (FUSED) {
+      // lane h holds d = 32t + 8i + 4h + (0..3) of its query; one 32-lane swap
+      // per pair of i gives it 8 consecutive values instead, so each store
+      // writes 16 whole bytes (d = 32t + 16p + 8h ..) of the row. The swap
+      // needs both lanes of a row, which are valid or not together.
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      bf16* op = Out + r * D + 4 * h;
+      bf16* op = Out + r * D + 8 * h;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x4 y = {to_bf16(o[t][4 * i + 0] * inv), to_bf16(o[t][4 * i + 1] * inv),
-                      to_bf16(o[t][4 * i + 2] * inv), to_bf16(o[t][4 * i + 3] * inv)};
-          *(bf16x4*)(op + 32 * t + 8 * i) = y;
+        for (int pp = 0; pp < 2; ++pp) {
+          const bf16x4 ya = {to_bf16(o[t][8 * pp + 0] * inv), to_bf16(o[t][8 * pp + 1] * inv),
+                             to_bf16(o[t][8 * pp + 2] * inv), to_bf16(o[t][8 * pp + 3] * inv)};
+          const bf16x4 yb = {to_bf16(o[t][8 * pp + 4] * inv), to_bf16(o[t][8 * pp + 5] * inv),
+                             to_bf16(o[t][8 * pp + 6] * inv), to_bf16(o[t][8 * pp + 7] * inv)};
+          const u32x2 a = __builtin_bit_cast(u32x2, ya), b = __builtin_bit_cast(u32x2, yb);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+          const u32x4 chunk = {s0[0], s1[0], s0[1], s1[1]};
+          if (qvalid) *(u32x4*)(op + 32 * t + 16 * pp) = chunk;
         }
-      if (Lse && h == 0) Lse[r] = lsum > 0.f ? (mu + fast_log2(lsum)) * kLn2 : kNegInf;
+      if (qvalid && Lse && h == 0) Lse[r] = lsum > 0.f ? (mu + fast_log2(lsum)) * kLn2 : kNegInf;
     } else {
+      if (!qvalid) return;
       float* op = Oacc + r * D + 4 * h;
 #pragma unroll
       for (int t = 0; t < DT; ++t)
