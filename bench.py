@@ -386,6 +386,40 @@ def cpu_baseline(w, rank, segs, budget_s):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def cpu_full_configs():
+    """The oracle, as it stands, on the three small configurations in full:
+    the tiny fp32 ring and the causal two-rank share (every rank's queries
+    against the whole sequence, the result their rings reach), and factored
+    spatial and temporal attention of the 16 x 900 video workload."""
+    import oracle
+    out = []
+    for w in (configs.TINY_F32, configs.CAUSAL_2RANK):
+        pos = np.arange(w.S)
+        t0 = time.perf_counter()
+        for b in range(w.B):
+            for h in range(w.H):
+                q, k, v = (seeded.exact_f64(seeded.to_dtype(seeded.normal_rows(w.wid, t, b, h, 0, w.S, w.d), w.dtype))
+                           for t in (seeded.Q, seeded.K, seeded.V))
+                oracle.attention_rows(q, pos, k, v, pos, w.scale, w.causal)
+        el = time.perf_counter() - t0
+        pairs = w.S * (w.S + 1) // 2 if w.causal else w.S * w.S
+        fl = sizing.attention_flop(pairs, w.d, w.B * w.H)
+        out.append({"workload": f"{w.name}, all {w.P} ranks' queries", "s": el, "TFLOP/s": fl / el / 1e12})
+    v = configs.VIDEO_FACTORED
+    for name, fn, pairs in (("spatial", oracle.factored_spatial, v.T * v.S_sp * v.S_sp),
+                            ("temporal", oracle.factored_temporal, v.S_sp * v.T * v.T)):
+        t0 = time.perf_counter()
+        for b in range(v.B):
+            for h in range(v.H):
+                q, k, vv = (seeded.exact_f64(seeded.to_dtype(seeded.normal_rows(v.wid, t, b, h, 0, v.N, v.d), v.dtype))
+                            for t in (seeded.Q, seeded.K, seeded.V))
+                fn(q, k, vv, v.T, v.S_sp, v.scale)
+        el = time.perf_counter() - t0
+        fl = sizing.attention_flop(pairs, v.d, v.B * v.H)
+        out.append({"workload": f"{v.name} {name}", "s": el, "TFLOP/s": fl / el / 1e12})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -496,6 +530,7 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle for ~{args.cpu_budget:.0f} s")
         rec["cpu_baseline"] = cpu_baseline(w, args.rank, segs, args.cpu_budget)
+        rec["cpu_baseline"]["full_configs"] = cpu_full_configs()
     print(json.dumps(rec), flush=True)
 
 

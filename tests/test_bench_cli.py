@@ -28,3 +28,15 @@ def test_cpu_baseline_leg_reports_its_sample():
     full_rows = w.B * w.H * w.L
     assert abs(rec["extrapolated_full_s"] - full_rows / rec["rows_per_s"]) < 1e-9 * rec["extrapolated_full_s"] + 1e-12
     assert "extrapolated" in rec["extrapolation"] and "query rows" in rec["sample"]
+
+
+def test_cpu_full_configs_time_the_small_workloads_in_full():
+    # the oracle in full on the tiny ring, the two-rank causal share and the
+    # factored video workload (about 10 s of host work)
+    sys.path.insert(0, ROOT)
+    import bench
+    recs = bench.cpu_full_configs()
+    names = [r["workload"] for r in recs]
+    assert any("tiny-f32-ring" in n for n in names) and any("causal-bf16-4k-cp2" in n for n in names)
+    assert any(n.endswith("spatial") for n in names) and any(n.endswith("temporal") for n in names)
+    assert all(r["s"] > 0 and r["TFLOP/s"] > 0 for r in recs)
