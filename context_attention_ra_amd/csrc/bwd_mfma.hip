@@ -318,7 +318,10 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(
 // dK, dV: owned keys, streamed Q/dO tiles. Eight waves (256 owned keys): the
 // owned V rows sit in LDS (four 64-row tiles of the same layout) and are read
 // as B operands, which keeps a wave within 256 registers, so two waves share
-// each SIMD and one's exponentials overlap the other's products.
+// each SIMD. (The dQ kernel's ping-pong does not pay here: the scores of a
+// whole next tile do not fit beside the two accumulators, and with half-tile
+// units each matrix phase reads about as many LDS bytes per product as the
+// LDS delivers.)
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
