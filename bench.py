@@ -424,7 +424,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=configs.LLM_32K_CP4.name, choices=sorted(configs.RING_WORKLOADS))
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-prefetch", action="store_true", help="pass each block on the compute stream")
