@@ -537,19 +537,20 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   // before the rounding, so that lse keeps full precision)
   auto exps = [&](float& tsum) RA_INLINE {
     const float mus = mu == kNegInf ? 0.f : mu;
-    float s0 = 0.f, s1 = 0.f;
+    float pr[16 * kNST];
 #pragma unroll
     for (int st = 0; st < kNST; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(__builtin_fmaf(sc[st][r], c_log2, -mus));
-        if (r & 1)
-          s1 += pr;
-        else
-          s0 += pr;
-        pf[2 * st + r / 8][r % 8] = to_bf16(pr);
+        pr[16 * st + r] = fast_exp2(__builtin_fmaf(sc[st][r], c_log2, -mus));
+        pf[2 * st + r / 8][r % 8] = to_bf16(pr[16 * st + r]);
       }
-    tsum = s0 + s1;
+    // pairwise sum: five dependent adds instead of a chain of sixteen
+#pragma unroll
+    for (int n = 8 * kNST; n >= 1; n /= 2)
+#pragma unroll
+      for (int i = 0; i < n; ++i) pr[i] = pr[2 * i] + pr[2 * i + 1];
+    tsum = pr[0];
   };
 
   // The matrix phase of one tile in a fixed order: the score MFMAs of the next
@@ -599,7 +600,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     if (ti.mask) apply_mask(ti);
     float tsum;
     exps(tsum);
-    const bool check = !(tsum <= kSumMax) || (mu == kNegInf && tsum > 0.f);
+    // bitwise, so that the test is two compares and lane-mask logic, not branches
+    const bool check = (!(tsum <= kSumMax)) | ((mu == kNegInf) & (tsum > 0.f));
     if (__builtin_amdgcn_ballot_w64(check)) {
       rescale(rowmax());
       exps(tsum);
