@@ -148,7 +148,7 @@ def run_bwd(q: torch.Tensor,
             scale: Optional[float] = None,
             order: Optional[List[int]] = None,
             dkv: Optional[List[Tuple[torch.Tensor, torch.Tensor]]] = None,
-            overlap: bool = False):
+            overlap: Optional[bool] = None):
     """Backward pass of rank `rank`'s share: P backward block steps.
 
     The ring passes the K/V blocks again in the backward pass (k8ai
@@ -164,7 +164,13 @@ def run_bwd(q: torch.Tensor,
     overlap    run the dK/dV half of every step on a second stream, beside the
                chain of dQ halves on the current stream (each block's dK/dV
                depends on no other step), and make the current stream wait for
-               it before returning; the gradients are bitwise the same
+               it before returning; the gradients are bitwise the same. None
+               (the default): only when the blocks have fewer K/V heads than
+               q has heads. Then the dK/dV kernel is a single round of
+               workgroups whose causal imbalance leaves CUs idle, which the
+               other stream's dQ workgroups fill; with one K/V head per query
+               head the two kernels only trade CUs and the second stream is
+               slower
     returns (dq [B, H, Lq, d] fp32, dkv)
     """
     P = len(kv_blocks)
@@ -177,6 +183,8 @@ def run_bwd(q: torch.Tensor,
     if scale is None:
         scale = 1.0 / d ** 0.5
     stream = torch.cuda.current_stream(dev)
+    if overlap is None:
+        overlap = kv_blocks[0][0].shape[1] < H
     fresh = dkv is None
     if fresh:
         dkv = [(torch.empty(k.shape, dtype=torch.float32, device=dev),
