@@ -438,6 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   typedef bf16x8 Probs[2 * kNST];  // [16-key slice]
   Scores sc;
   Probs pf;
+  Scores pw;  // the weights in fp32, rounded to pf inside the matrix phase
 
   auto scores = [&](int stage) RA_INLINE {
     const char* kb = smem + stage * L::STAGE + kread;
@@ -532,9 +533,10 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     }
   };
 
-  // exponentials of one tile against the current reference, into bf16 B
-  // operands; tsum gets this lane's share of the tile's row sum (in fp32,
-  // before the rounding, so that lse keeps full precision)
+  // exponentials of one tile against the current reference, into the fp32
+  // weights pw (rounded to the bf16 B operands pf in the next matrix phase);
+  // tsum gets this lane's share of the tile's row sum (in fp32, before the
+  // rounding, so that lse keeps full precision)
   auto exps = [&](float& tsum) RA_INLINE {
     const float mus = mu == kNegInf ? 0.f : mu;
     float pr[16 * kNST];
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         pr[16 * st + r] = fast_exp2(__builtin_fmaf(sc[st][r], c_log2, -mus));
-        pf[2 * st + r / 8][r % 8] = to_bf16(pr[16 * st + r]);
+        pw[st][r] = pr[16 * st + r];
       }
     // pairwise sum: five dependent adds instead of a chain of sixteen
 #pragma unroll
@@ -585,6 +587,14 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[kc], o[t], 0, 0, 0);
       }
       if (i + kAhead < NSC + NPV) op[i % kAhead] = operand(i + kAhead);
+      // the bf16 weights of slice kc, rounded between the first score products
+      // (the matrix wave has issue slots to spare there; the vector phase
+      // of the other wave does not)
+      if (i >= 1 && i < 1 + 2 * kNST) {
+        const int kc = i - 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[kc][e] = to_bf16(pw[kc / 2][8 * (kc % 2) + e]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -610,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     // the weights are complete here: without this use the compiler sinks part
     // of the exponentials and conversions past the barrier into the other
     // phase, where the same wave then issues them between its products
-    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]), "v"(lpart[0]), "v"(lpart[1]));
+    asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(lpart[0]), "v"(lpart[1]));
   };
 
   // ---- ping-pong schedule, one item at a time. The two halves of the
