@@ -317,8 +317,8 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // dK, dV: owned keys, streamed Q/dO tiles. Eight waves (256 owned keys): the
 // owned V rows sit in LDS (four 64-row tiles of the same layout) and are read
-// as B operands, which keeps a wave within 256 registers, so two waves share
-// each SIMD. (The dQ kernel's ping-pong does not pay here: the scores of a
+// as B operands (half of their k-steps from registers), which keeps a wave
+// within 256 registers, so two waves share each SIMD. (The dQ kernel's ping-pong does not pay here: the scores of a
 // whole next tile do not fit beside the two accumulators, and with half-tile
 // units each matrix phase reads about as many LDS bytes per product as the
 // LDS delivers.)
@@ -424,6 +424,13 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   store_rowv(0);
   __syncthreads();
+  // the first half of the k-steps of this wave's owned V rows stay in
+  // registers (as many as fit beside the accumulators), which spares the
+  // LDS a quarter of its row reads
+  constexpr int NVR = KS / 2;
+  bf16x8 vf[NVR];
+#pragma unroll
+  for (int s = 0; s < NVR; ++s) vf[s] = row_operand<D>(vw, w & 1, s, l32, h);
   for (int32_t n = 0; n < ntiles; ++n) {
     if (n + 1 < ntiles) {
       fetch_rowv(n + 1);
@@ -447,8 +454,9 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int ksi = 0; ksi < KS; ++ksi) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qt, st, ksi, l32, h), kf[ksi], s, 0, 0, 0);
-        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(dt, st, ksi, l32, h),
-                                                      row_operand<D>(vw, w & 1, ksi, l32, h), dpv, 0, 0, 0);
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            row_operand<D>(dt, st, ksi, l32, h), ksi < NVR ? vf[ksi] : row_operand<D>(vw, w & 1, ksi, l32, h),
+            dpv, 0, 0, 0);
       }
       // masked scores become -inf (weight exactly 0) in one block, so that
       // the exponentials below are straight-line code
