@@ -140,6 +140,12 @@ STEP_CASES = [
     (2, 2, 190, [(64, 190)], 161, [(0, 161)], 64, True, torch.float32),
     (1, 3, 77, [(10, 40), (300, 37)], 250, [(0, 120), (200, 130)], 128, True, torch.float32),
     (1, 1, 96, [(0, 96)], 33, [(5, 33)], 128, False, torch.float32),
+    # degenerate sizes: one query against one key, one query against a block
+    # one key longer than a tile, and a single key seen by every query (the
+    # output is that key's value row)
+    (1, 2, 1, [(5, 1)], 1, [(3, 1)], 128, True, torch.bfloat16),
+    (1, 1, 1, [(0, 1)], 65, [(0, 65)], 64, False, torch.bfloat16),
+    (3, 1, 33, [(100, 33)], 1, [(50, 1)], 128, True, torch.float32),
 ]
 
 
