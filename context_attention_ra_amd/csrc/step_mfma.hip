@@ -710,7 +710,11 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     if (!more) break;
     cc = nx;
     begin_item();
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // the state just requested must be in. Without state nothing is pending
+    // but the output stores, which no wait here needs: the counter is in
+    // order, so the first tile wait of the next item covers them, a slot or
+    // two after they were issued
+    if (MODE != kAttend) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   }
   };
