@@ -516,6 +516,13 @@ def main():
     with_pf, without_pf = (ms2, ms_per_step) if cmp_prefetch else (ms_per_step, ms2)
     # share of the serial pass time that passing the blocks on the side stream saves
     rec["prefetch_saving"] = (without_pf - with_pf) / without_pf
+    if not args.no_prefetch:
+        # in the timed passes the block copy runs beside the step kernels and
+        # shares the GPU with them; the comparison passes run each kernel alone
+        alone = (total / w.P) / (float(kms2.mean()) * 1e-3)
+        rec["roofline"]["frac_kernel_alone"] = alone / PEAK_BF16_DENSE
+        rec["roofline"]["kernel_alone_timing"] = ("the same launches in the comparison passes (blocks passed on the "
+                                                  "compute stream, no copy beside the kernel)")
     if not args.no_legs:
         log("[bench] legs: merge, factored spatial, factored temporal")
         rec["legs"] = legs(w, q, dev, reps=20)

@@ -86,8 +86,9 @@ ra_status step_args(const void* q, const void* k, const void* v, ra_dtype dt, in
   if (!supported_d(d)) return RA_ERR_UNSUPPORTED;
   const int64_t tiles = (int64_t)nb * ((Lq + 127) / 128);
   if (tiles > (int64_t)INT32_MAX / 2) return RA_ERR_UNSUPPORTED;
-  // one (batch, head) slice of K or V must be addressable by a 32-bit offset
+  // one (batch, head) slice of Q, K or V must be addressable by a 32-bit offset
   if ((int64_t)Lk * d * (int64_t)es > (int64_t)INT32_MAX) return RA_ERR_UNSUPPORTED;
+  if ((int64_t)Lq * d * (int64_t)es > (int64_t)INT32_MAX) return RA_ERR_UNSUPPORTED;
 
   ra::StepArgs& a = *out_args;
   a = ra::StepArgs{};
@@ -339,6 +340,11 @@ ra_status ra_kv_pass(const void* k_src, const void* v_src, void* k_dst, void* v_
               e = span(v_dst, bytes);
   if (overlap(c, e) || overlap(c, a) || overlap(c, b) || overlap(e, a) || overlap(e, b))
     return RA_ERR_INVALID_ARG;
+  // the pass kernel (sized to run beside a ring step) for 16-byte aligned
+  // buffers of whole 16-byte pieces; the runtime's copy otherwise
+  if (aligned(k_src, 16) && aligned(v_src, 16) && aligned(k_dst, 16) && aligned(v_dst, 16) &&
+      bytes % 16 == 0 && bytes / 16 <= ((size_t)1 << 30))
+    return hip_fail(ra::launch_kv_pass(k_src, k_dst, v_src, v_dst, (int64_t)(bytes / 16), stream));
   hipError_t err = hipMemcpyAsync(k_dst, k_src, bytes, hipMemcpyDeviceToDevice, stream);
   if (err == hipSuccess) err = hipMemcpyAsync(v_dst, v_src, bytes, hipMemcpyDeviceToDevice, stream);
   return hip_fail(err);

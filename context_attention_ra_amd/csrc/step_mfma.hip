@@ -135,13 +135,17 @@ struct Cursor {
 //           step with the finalize folded in (the state is left unchanged).
 enum Mode { kStep = 0, kAttend = 1, kLast = 2 };
 
+#define RA_STEP_PARAMS                                                                        \
+  const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,         \
+      int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, int32_t init, \
+      float *__restrict__ Oacc, float *__restrict__ Mst, float *__restrict__ Lst,             \
+      bf16 *__restrict__ Out, float *__restrict__ Lse, int32_t nqt, int32_t per_xcd,          \
+      int32_t nwg_x, int32_t group
+#define RA_STEP_ARGS \
+  Q, K, V, nb, Lq, Lk, qs, ks, c_log2, init, Oacc, Mst, Lst, Out, Lse, nqt, per_xcd, nwg_x, group
+
 template <int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    int32_t nb, int32_t Lq, int32_t Lk, DevSegs qs, DevSegs ks, float c_log2, int32_t init,
-    float* __restrict__ Oacc, float* __restrict__ Mst, float* __restrict__ Lst,
-    bf16* __restrict__ Out, float* __restrict__ Lse, int32_t nqt, int32_t per_xcd, int32_t nwg_x,
-    int32_t group) {
+__device__ __forceinline__ void step_mfma_body(RA_STEP_PARAMS) {
   using L = Lay<D>;
   constexpr int KS = D / 16;  // k-steps of the score MFMA
   constexpr int DT = D / 32;  // 32-wide output tiles
@@ -313,7 +317,11 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
   bf16x8 qf[KS];
   auto load_q = [&](const Item& it) RA_INLINE {
     const int32_t row = min(it.qt0 + 32 * w + l32, Lq - 1);
-    const bf16* qp = Q + ((size_t)it.prob * Lq + row) * D + 8 * h;
+    // in the non-final steps the lane's part as a 32-bit offset (a slice of Q
+    // is under 2 GiB), one VGPR instead of a 64-bit lane pointer kept across
+    // the item loop; the other modes keep the form they were tuned with
+    const bf16* qp = MODE == kStep ? (Q + (size_t)it.prob * Lq * D) + (row * D + 8 * h)
+                                   : Q + ((size_t)it.prob * Lq + row) * D + 8 * h;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
   };
@@ -724,6 +732,32 @@ __global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(
     run(BoolC<false>{});
   if (MODE == kLast && state_in) finalize_empty_items();
 }
+
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void step_mfma_kernel(RA_STEP_PARAMS) {
+  step_mfma_body<D, CAUSAL, MODE>(RA_STEP_ARGS);
+}
+
+// The steps before the last one of a ring run while the next block is passed
+// on a side stream. Two waves of 248 VGPRs leave 16 registers per SIMD lane,
+// where one wave of the block-pass copy kernel fits beside the step kernel;
+// with 251-256 the SIMD's register file is full and the copy only runs in the
+// step kernel's tail, after its workgroups finish. On gfx950 the attribute
+// counts the unified VGPR/AGPR file in pairs: 124 caps the kernel at 248.
+// (At d = 64 the kernel needs about 200.)
+template <>
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_num_vgpr(124))) void
+step_mfma_kernel<128, true, kStep>(RA_STEP_PARAMS) {
+  step_mfma_body<128, true, kStep>(RA_STEP_ARGS);
+}
+template <>
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_num_vgpr(124))) void
+step_mfma_kernel<128, false, kStep>(RA_STEP_PARAMS) {
+  step_mfma_body<128, false, kStep>(RA_STEP_ARGS);
+}
+
+#undef RA_STEP_PARAMS
+#undef RA_STEP_ARGS
 
 DevSegs dev(const HostSegs& s) { return DevSegs{s.start0, s.start1, s.len0, s.len}; }
 

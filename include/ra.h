@@ -103,9 +103,10 @@ typedef struct ra_segs {
  * dt: RA_BF16 (matrix-core path) or RA_F32 (fp32 vector path).
  * Errors: RA_ERR_INVALID_ARG for null pointers, B/H/Lq/Lk <= 0, bad segments,
  *   a non-finite or non-positive scale, unknown flags or mask, or o_acc/m/l
- *   overlapping q/k/v; RA_ERR_UNSUPPORTED for d not in {64, 128}, a K/V
- *   slice (Lk * d elements) of more than INT32_MAX bytes, or more than 2^30
- *   (batch x head, 128-row query tile) pairs.
+ *   overlapping q/k/v; RA_ERR_UNSUPPORTED for d not in {64, 128}, a Q
+ *   slice (Lq * d elements) or K/V slice (Lk * d elements) of more than
+ *   INT32_MAX bytes, or more than 2^30 (batch x head, 128-row query tile)
+ *   pairs.
  */
 ra_status ra_step(const void* q, const void* k, const void* v, ra_dtype dt,
                   int32_t B, int32_t H, int32_t Lq, int32_t Lk, int32_t d,
@@ -295,7 +296,11 @@ ra_status ra_factored_temporal(const void* q, const void* k, const void* v, ra_d
  * computing on the current one). On one GPU the transfer from the source rank
  * is simulated by an asynchronous device-to-device copy of its K and V blocks
  * into the receive buffers, enqueued on `stream` (normally a side stream, so
- * the copy overlaps the current step's compute).
+ * the copy overlaps the current step's compute). For 16-byte aligned buffers
+ * of a multiple of 16 bytes (up to 16 GiB) the copy is the library's pass
+ * kernel, whose waves are small enough (16 VGPRs) to run on every SIMD beside
+ * the kernel of ra_step and ra_step_gqa, which leaves room for one; other
+ * buffers take the runtime's device-to-device copy.
  * k_src, v_src -> k_dst, v_dst: `bytes` each, device memory; source and
  * destination must not overlap. bytes == 0 is a no-op.
  */

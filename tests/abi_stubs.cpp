@@ -45,6 +45,7 @@ hipError_t launch_add_rows(const float*, int64_t, int64_t, float*, int64_t, int6
                            hipStream_t) {
   return counted();
 }
+hipError_t launch_kv_pass(const void*, void*, const void*, void*, int64_t, hipStream_t) { return counted(); }
 hipError_t launch_step_bwd_bf16(const BwdArgs&, hipStream_t) { return counted(); }
 hipError_t launch_bwd_prep_bf16(const void*, const void*, int64_t, int32_t, float*, hipStream_t) {
   return counted();

@@ -84,6 +84,8 @@ INV, UNS = _lib.RA_ERR_INVALID_ARG, _lib.RA_ERR_UNSUPPORTED
     (dict(o=ptr(0)), INV),  # state overlapping the queries
     (dict(m=ptr(3)), INV),  # m overlapping o_acc
     (dict(d=96), UNS), (dict(d=256), UNS),
+    # a query slice past 32-bit byte offsets (2^23 rows of 128 bf16 values)
+    (dict(Lq=1 << 23, qs=((0, 1 << 23),)), UNS),
 ])
 def test_step_rejects_bad_arguments(lib, kw, expect):
     assert step(lib, **kw) == expect
