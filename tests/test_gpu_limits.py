@@ -7,8 +7,9 @@ overflow would show. One head of 2^23 - 64 query rows (just under 2 GiB of
 bf16) attends to one 64-key block; the first and last rows of the slice are
 checked against the oracle (the definition of attention, Day 83 post,
 "Context parallelism: splitting the sequence"), with and without the causal
-mask. Inputs are drawn on the GPU with a seeded generator; the checked rows
-are read back and given to the oracle as they are.
+mask. A second test runs the largest K/V slice (2^23 - 64 keys) against a
+closed form. Inputs are drawn on the GPU with a seeded generator; the checked
+rows are read back and given to the oracle as they are.
 """
 
 import numpy as np
@@ -60,4 +61,49 @@ def test_largest_query_slice_step(gpu_lib, causal):
     assert np.all(np.isfinite(rl)), "every checked row sees a key"
     assert_close(out, ro, lse, rl, torch.bfloat16, f"largest slice causal={causal}")
     del q, st
+    torch.cuda.empty_cache()
+
+
+def test_largest_kv_slice_step(gpu_lib):
+    """One block of 2^23 - 64 keys (just under 2 GiB of bf16 per tensor): all
+    keys are zero (score 0) except the last 64, which are small random
+    directions, so the expected output has a closed form that a chunked fp64
+    sum over V computes: out_i = (sum_j w_ij v_j) / (sum_j w_ij) with w_ij = 1
+    for the plain keys and exp(s_ij) for the last 64."""
+    LKB, LQB = (1 << 23) - 64, 64
+    banner(f"ra_step over a block of {LKB} keys")
+    assert LKB * D * 2 <= 2**31 - 1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    q = torch.randn((1, 1, LQB, D), device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn((1, 1, LKB, D), device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.zeros((1, 1, LKB, D), device="cuda", dtype=torch.bfloat16)
+    # the last 64 keys: small random directions (scores of about a quarter)
+    k[0, 0, LKB - 64:] = (0.25 * torch.randn((64, D), device="cuda", generator=g)).to(torch.bfloat16)
+    st = ring.RingState(1, 1, LQB, D, "cuda")
+    scale = D ** -0.5
+    _lib.ra_step(q, k, v, [(0, LQB)], [(0, LKB)], False, scale, st.o, st.m, st.l, init=True)
+    torch.cuda.synchronize()
+    o = st.o[0, 0].double().cpu().numpy()
+    m = st.m[0, 0].double().cpu().numpy()
+    l = st.l[0, 0].double().cpu().numpy()
+    out, lse = o / l[:, None], m + np.log(l)
+    # closed form: the plain keys contribute weight 1 each and their V rows' sum
+    qc = seeded.exact_f64(q[0, 0].cpu())
+    kt = seeded.exact_f64(k[0, 0, LKB - 64:].cpu())
+    vt = seeded.exact_f64(v[0, 0, LKB - 64:].cpu())
+    vsum = np.zeros(D)
+    step = 1 << 20
+    for r0 in range(0, LKB - 64, step):
+        r1 = min(r0 + step, LKB - 64)
+        vsum += seeded.exact_f64(v[0, 0, r0:r1].cpu()).sum(axis=0)
+    s = scale * (qc @ kt.T)                       # [LQB, 64]
+    smax = np.maximum(s.max(axis=1), 0.0)
+    wt = np.exp(s - smax[:, None])
+    w0 = np.exp(-smax) * (LKB - 64)               # the plain keys' total weight
+    den = w0 + wt.sum(axis=1)
+    ro = (np.exp(-smax)[:, None] * vsum[None, :] + wt @ vt) / den[:, None]
+    rl = smax + np.log(den)
+    assert_close(out, ro, lse, rl, torch.bfloat16, "largest block")
+    del k, v, st
     torch.cuda.empty_cache()
