@@ -7,9 +7,10 @@ overflow would show. One head of 2^23 - 64 query rows (just under 2 GiB of
 bf16) attends to one 64-key block; the first and last rows of the slice are
 checked against the oracle (the definition of attention, Day 83 post,
 "Context parallelism: splitting the sequence"), with and without the causal
-mask. A second test runs the largest K/V slice (2^23 - 64 keys) against a
-closed form. Inputs are drawn on the GPU with a seeded generator; the checked
-rows are read back and given to the oracle as they are.
+mask. Further tests run the largest K/V slice (2^23 - 64 keys) against a
+closed form, and the backward step over the largest query slice. Inputs are
+drawn on the GPU with a seeded generator; the checked rows are read back and
+given to the oracle as they are.
 """
 
 import numpy as np
@@ -19,7 +20,7 @@ import torch
 import oracle
 import seeded
 from context_attention_ra_amd import _lib, ring
-from ringcase import assert_close
+from ringcase import assert_close, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -106,4 +107,57 @@ def test_largest_kv_slice_step(gpu_lib):
     rl = smax + np.log(den)
     assert_close(out, ro, lse, rl, torch.bfloat16, "largest block")
     del k, v, st
+    torch.cuda.empty_cache()
+
+
+def grad_close(gpu, ref, what):
+    """Gradients relative to their own scale (max |ref|) and in aggregate."""
+    mx, mr = compare(gpu, ref)
+    sc = max(float(np.abs(ref).max()), 1e-30)
+    msg = f"{what}: max_abs={mx:.3e} (max|ref|={sc:.3e}) mean_rel={mr:.3e}"
+    print(msg, flush=True)
+    assert mx <= 2e-2 * sc and mr <= 1e-2, msg
+
+
+def test_largest_query_slice_backward(gpu_lib):
+    """The backward step over the largest query slice against one 64-key
+    block. The upstream gradient is zero except on the first and last rows, so
+    dk and dv, sums over all 2^23 - 64 queries that the dK/dV kernel streams
+    to the end of the slice, equal the oracle's gradients of those rows alone;
+    dq of those rows is checked too, and dq of a row with zero upstream
+    gradient must be exactly zero."""
+    banner(f"ra_step_bwd over {LQ} query rows")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4048)
+    q = torch.randn((1, 1, LQ, D), device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn((1, 1, LK, D), device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn((1, 1, LK, D), device="cuda", generator=g).to(torch.bfloat16)
+    rows = np.concatenate([np.arange(EDGE), np.arange(LQ - EDGE, LQ)])
+    ri = torch.as_tensor(rows, device="cuda")
+    do = torch.zeros((1, 1, LQ, D), device="cuda", dtype=torch.bfloat16)
+    do[0, 0].index_copy_(0, ri, torch.randn((len(rows), D), device="cuda", generator=g).to(torch.bfloat16))
+    runs_q, runs_k = [(0, LQ)], [(0, LK)]
+    scale = D ** -0.5
+    st = ring.RingState(1, 1, LQ, D, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 1, LQ), dtype=torch.float32, device="cuda")
+    _lib.ra_step_final(q, k, v, runs_q, runs_k, False, scale, st.o, st.m, st.l, out, lse, init=True)
+    del st
+    delta = torch.empty_like(lse)
+    _lib.ra_bwd_prep(out, do, delta)
+    del out
+    dq = torch.empty((1, 1, LQ, D), dtype=torch.float32, device="cuda")
+    dk = torch.empty((1, 1, LK, D), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    _lib.ra_step_bwd(q, k, v, do, lse, delta, runs_q, runs_k, False, scale, dq, dk, dv, init_dq=True, init_dkv=True)
+    torch.cuda.synchronize()
+    kc, vc = (seeded.exact_f64(t[0, 0].cpu()) for t in (k, v))
+    qs, dos = (seeded.exact_f64(t[0, 0].index_select(0, ri).cpu()) for t in (q, do))
+    rq, rk, rv = oracle.attention_grads(qs, rows, kc, vc, np.arange(LK), scale, False, dos)
+    grad_close(dq[0, 0].index_select(0, ri).double().cpu().numpy(), rq, "largest slice dq")
+    grad_close(dk[0, 0].double().cpu().numpy(), rk, "largest slice dk")
+    grad_close(dv[0, 0].double().cpu().numpy(), rv, "largest slice dv")
+    mid = torch.as_tensor([EDGE, LQ // 2, LQ - EDGE - 1], device="cuda")
+    assert bool((dq[0, 0].index_select(0, mid) == 0).all()), "rows with zero upstream gradient"
+    del q, do, dq
     torch.cuda.empty_cache()
