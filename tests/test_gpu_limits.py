@@ -8,7 +8,8 @@ bf16) attends to one 64-key block; the first and last rows of the slice are
 checked against the oracle (the definition of attention, Day 83 post,
 "Context parallelism: splitting the sequence"), with and without the causal
 mask. Further tests run the largest K/V slice (2^23 - 64 keys) against a
-closed form, and the backward step over the largest query slice. Inputs are
+closed form, the backward step over the largest query slice, and factored
+temporal attention over the largest long-clip slice. Inputs are
 drawn on the GPU with a seeded generator; the checked rows are read back and
 given to the oracle as they are.
 """
@@ -160,4 +161,33 @@ def test_largest_query_slice_backward(gpu_lib):
     mid = torch.as_tensor([EDGE, LQ // 2, LQ - EDGE - 1], device="cuda")
     assert bool((dq[0, 0].index_select(0, mid) == 0).all()), "rows with zero upstream gradient"
     del q, do, dq
+    torch.cuda.empty_cache()
+
+
+def test_largest_temporal_slice(gpu_lib):
+    """Factored temporal attention of the longest clip (128 frames) with the
+    largest slice the long-clip kernel accepts (T * S_sp * d bf16 values just
+    under 2 GiB): the temporal attention at a spatial position is plain
+    attention among its T tokens, so each checked position's rows are taken
+    out and given to the oracle as a clip of one position."""
+    T = 128
+    S_sp = (2**31 - 1) // (T * D * 2)
+    N = T * S_sp
+    banner(f"ra_factored_temporal, T={T} S_sp={S_sp} ({N} tokens)")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(128)
+    q, k, v = (torch.randn((1, 1, N, D), device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 1, N), dtype=torch.float32, device="cuda")
+    scale = D ** -0.5
+    _lib.ra_factored_temporal(q, k, v, T, S_sp, scale, out, lse)
+    torch.cuda.synchronize()
+    for s in (0, 1, S_sp // 2, S_sp - 2, S_sp - 1):
+        ri = torch.arange(T, device="cuda") * S_sp + s
+        qc, kc, vc = (seeded.exact_f64(t[0, 0].index_select(0, ri).cpu()) for t in (q, k, v))
+        ro, rl = oracle.factored_temporal(qc, kc, vc, T, 1, scale)
+        assert_close(out[0, 0].index_select(0, ri).double().cpu().numpy(), ro,
+                     lse[0, 0].index_select(0, ri).double().cpu().numpy(), rl, torch.bfloat16,
+                     f"largest temporal slice, position {s}")
+    del q, k, v, out
     torch.cuda.empty_cache()
