@@ -1,0 +1,69 @@
+"""A whole ring pass captured in a HIP graph replays bitwise like eager passes.
+
+The ring driver launches every kernel on the caller's current stream and the
+block pass on a side stream forked from it and joined back through events,
+and nothing on the path clears memory with a memset, so one pass of
+`ring.run` can be captured (torch.cuda.CUDAGraph) and replayed. The replays
+are compared with the eager pass on the same inputs, with eager passes run
+between them (the causal two-rank share, rank 0, and the same share with
+grouped K/V heads).
+"""
+
+import pytest
+import torch
+
+from context_attention_ra_amd import configs, layout, ring
+import seeded
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(w, dev):
+    import numpy as np
+    segs = [layout.split(w.split, w.S, w.P, t) for t in range(w.P)]
+    pos = [np.concatenate([np.arange(s, s + n) for s, n in sg]) for sg in segs]
+    q = seeded.gen_bhsd_at(w.wid, seeded.Q, w.B, w.H, pos[0], w.d, w.dtype, dev)
+    kv = [(seeded.gen_bhsd_at(w.wid, seeded.K, w.B, w.Hkv, pos[t], w.d, w.dtype, dev),
+           seeded.gen_bhsd_at(w.wid, seeded.V, w.B, w.Hkv, pos[t], w.d, w.dtype, dev)) for t in range(w.P)]
+    return q, segs, kv
+
+
+@pytest.mark.parametrize("wname", ["causal-bf16-4k-cp2", "causal-bf16-4k-cp2-gqa4"])
+def test_ring_pass_in_a_graph(gpu_lib, wname):
+    print(f"\n[graph] {wname}: one ring pass captured and replayed", flush=True)
+    w = configs.RING_WORKLOADS[wname]
+    dev = torch.device("cuda")
+    q, segs, kv = _inputs(w, dev)
+    st = ring.RingState(w.B, w.H, w.L, w.d, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+    bufs = [(torch.empty_like(kv[0][0]), torch.empty_like(kv[0][1])) for _ in range(2)]
+    side = torch.cuda.Stream(dev)
+
+    def one():
+        ring.run(q, segs[0], kv, segs, 0, w.causal, scale=w.scale, out=out, lse=lse, state=st, bufs=bufs,
+                 copy_stream=side)
+
+    one()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        one()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {rep}"
+        one()  # an eager pass between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"eager after replay {rep}"
