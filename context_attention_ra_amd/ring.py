@@ -148,7 +148,8 @@ def run_bwd(q: torch.Tensor,
             scale: Optional[float] = None,
             order: Optional[List[int]] = None,
             dkv: Optional[List[Tuple[torch.Tensor, torch.Tensor]]] = None,
-            overlap: Optional[bool] = None):
+            overlap: Optional[bool] = None,
+            split: bool = False):
     """Backward pass of rank `rank`'s share: P backward block steps.
 
     The ring passes the K/V blocks again in the backward pass (k8ai
@@ -171,6 +172,23 @@ def run_bwd(q: torch.Tensor,
                other stream's dQ workgroups fill; with one K/V head per query
                head the two kernels only trade CUs and the second stream is
                slower
+    split      on the step against the rank's own block (the diagonal: under
+               the causal mask its key tiles see very different numbers of
+               queries), run the dK/dV half as two launches on two streams,
+               each over half of every K/V head's query heads (the group,
+               H / H_kv, must be even), the second into a partial accumulator
+               that is then added in. With grouped heads the dK/dV grid has
+               one workgroup per key tile and K/V head, as many as there are
+               CUs at the 32K share, so the diagonal's heaviest tiles set that
+               kernel's time, and the halves cut it by 28%; but the whole pass
+               is not faster, since the dQ kernels on the other stream already
+               fill the CUs that the light tiles leave idle, and the copies of
+               the halves cost more than is left. Off by default. The
+               gradients equal the unsplit ones up to the order of the fp32
+               sums. Refused under graph capture: a captured pass with it (a
+               third stream forked from the dK/dV stream and joined back into
+               it) ended in a crash inside the runtime's end of capture whose
+               cause is not known
     returns (dq [B, H, Lq, d] fp32, dkv)
     """
     P = len(kv_blocks)
@@ -182,9 +200,15 @@ def run_bwd(q: torch.Tensor,
     dev = q.device
     if scale is None:
         scale = 1.0 / d ** 0.5
+    H_kv = kv_blocks[0][0].shape[1]
+    G = H // H_kv
+    if split and (G % 2 != 0 or G * H_kv != H):
+        raise ValueError("split needs an even number of query heads per K/V head")
     stream = torch.cuda.current_stream(dev)
+    if split and torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("the split diagonal step is not supported under graph capture")
     if overlap is None:
-        overlap = kv_blocks[0][0].shape[1] < H
+        overlap = H_kv < H
     fresh = dkv is None
     if fresh:
         dkv = [(torch.empty(k.shape, dtype=torch.float32, device=dev),
@@ -192,6 +216,23 @@ def run_bwd(q: torch.Tensor,
     delta = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
     _lib.ra_bwd_prep(out, dout, delta, stream=stream)
     dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device=dev)
+    halves = None
+    if split and rank in order:
+        # query head h belongs to K/V head h // G; half p holds the query
+        # heads G/2 * p .. G/2 * (p + 1) - 1 of every group, as contiguous
+        # copies, so K/V head j of a half serves its heads j*G/2 .. j*G/2+G/2-1
+        def half(x, p):
+            g = x.view(B, H_kv, G, *x.shape[2:])[:, :, p * (G // 2):(p + 1) * (G // 2)]
+            return g.reshape(B, H // 2, *x.shape[2:]).contiguous()
+        halves = [tuple(half(x, p) for x in (q, dout, lse, delta)) for p in (0, 1)]
+        # a stand-in of the right shape for the halves' dq argument, which the
+        # dK/dV-only launches neither read nor write
+        dq_unused = dq.view(-1)[:dq.numel() // 2].view(B, H // 2, Lq, d)
+        part = (torch.empty(kv_blocks[rank][0].shape, dtype=torch.float32, device=dev),
+                torch.empty(kv_blocks[rank][0].shape, dtype=torch.float32, device=dev))
+        split_stream = torch.cuda.Stream(dev)
+        for x in (*halves[1], *part, *kv_blocks[rank], dq):
+            x.record_stream(split_stream)
     side = None
     if overlap:
         side = torch.cuda.Stream(dev)
@@ -203,12 +244,27 @@ def run_bwd(q: torch.Tensor,
         for (k, v), (dk, dv) in zip(kv_blocks, dkv):
             for x in (k, v, dk, dv):
                 x.record_stream(side)
+        if halves is not None:
+            for x in (*halves[0], *part, dq):
+                x.record_stream(side)
     for s in range(P):
         t = order[s]
         k, v = kv_blocks[t]
         dk, dv = dkv[t]
         args = (q, k, v, dout, lse, delta, q_segs, kv_segs[t], causal, scale, dq, dk, dv)
-        if side is None:
+        if halves is not None and t == rank:
+            kv_stream = stream if side is None else side
+            split_stream.wait_stream(kv_stream)  # the halves, and earlier steps' writes to dk, dv
+            _lib.ra_step_bwd(*args, init_dq=(s == 0), init_dkv=fresh, stream=stream, parts="dq")
+            for p, (qh, doh, lh, dh) in enumerate(halves):
+                acc = (dk, dv) if p == 0 else part
+                _lib.ra_step_bwd(qh, k, v, doh, lh, dh, q_segs, kv_segs[t], causal, scale, dq_unused, *acc,
+                                 init_dkv=(fresh if p == 0 else True), parts="dkv",
+                                 stream=(kv_stream if p == 0 else split_stream))
+            kv_stream.wait_stream(split_stream)
+            _lib.ra_add_rows(part[0], 0, dk, 0, k.shape[2], stream=kv_stream)
+            _lib.ra_add_rows(part[1], 0, dv, 0, k.shape[2], stream=kv_stream)
+        elif side is None:
             _lib.ra_step_bwd(*args, init_dq=(s == 0), init_dkv=fresh, stream=stream)
         else:
             _lib.ra_step_bwd(*args, init_dq=(s == 0), init_dkv=fresh, stream=side, parts="dkv")

@@ -309,6 +309,31 @@ def test_ring_drivers_refuse_bad_block_orders():
             ring.run_bwd(q, segs[0], kv, segs, 0, True, q, torch.zeros((1, 1, 64)), q, order=order)
 
 
+def test_backward_split_needs_an_even_group():
+    # splitting the diagonal step's query heads in two halves per K/V head is
+    # refused on the host for an odd group (3 query heads per K/V head)
+    import torch
+    from context_attention_ra_amd import ring
+    q = torch.zeros((1, 3, 64, 64), dtype=torch.bfloat16)
+    kv = [(torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16),) * 2]
+    with pytest.raises(ValueError):
+        ring.run_bwd(q, [(0, 64)], kv, [[(0, 64)]], 0, True, q, torch.zeros((1, 3, 64)), q, split=True)
+
+
+def test_backward_split_refused_under_graph_capture(monkeypatch):
+    # the split diagonal step is refused while the current stream captures a
+    # graph (checked on the host before any buffer is made or call is made)
+    import torch
+    from context_attention_ra_amd import ring
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda dev=None: None)
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    monkeypatch.setattr(_lib, "load", lambda: (_ for _ in ()).throw(AssertionError("the library was reached")))
+    q = torch.zeros((1, 4, 64, 64), dtype=torch.bfloat16)
+    kv = [(torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16),) * 2]
+    with pytest.raises(RuntimeError):
+        ring.run_bwd(q, [(0, 64)], kv, [[(0, 64)]], 0, True, q, torch.zeros((1, 4, 64)), q, split=True)
+
+
 def test_binding_checks_dtypes_and_devices_before_any_library_call(monkeypatch):
     # The C calls derive every byte count from one dtype argument and cannot
     # tell host pointers from device ones: the binding must refuse mismatched

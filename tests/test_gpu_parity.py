@@ -882,6 +882,76 @@ def test_bwd_gqa_llm_32k_rank0_last_kv_head(gpu_lib):
         grad_close(dkv[t][1][0, g].cpu().double().numpy(), rv[0, kpos], f"dv block {t} kv head {g}")
 
 
+@pytest.mark.parametrize("G,B,L", [(2, 2, 1000), (4, 1, 777), (8, 1, 513)])
+def test_bwd_split_diagonal_step(gpu_lib, G, B, L):
+    # the causal diagonal step with its dK/dV half split over the two halves
+    # of every K/V head's query heads (two streams, the second half into a
+    # partial accumulator that is added in), against the unsplit step and the
+    # oracle, with fresh accumulators and with accumulators that already hold
+    # other ranks' sums; the dQ launches are the same, so dq is bitwise equal
+    Hkv, d, dt = 2, 128, torch.bfloat16
+    H = G * Hkv
+    banner(f"backward diagonal step split in head halves: B{B} H{H} H_kv{Hkv} L{L}")
+    wid = 600 + G
+    q = seeded.gen_bhsd(wid, seeded.Q, B, H, 0, L, d, dt, "cuda")
+    k = seeded.gen_bhsd(wid, seeded.K, B, Hkv, 0, L, d, dt, "cuda")
+    v = seeded.gen_bhsd(wid, seeded.V, B, Hkv, 0, L, d, dt, "cuda")
+    do = seeded.gen_bhsd(wid, DOUT, B, H, 0, L, d, dt, "cuda")
+    segs = [(0, L)]
+    scale = d ** -0.5
+    out, lse, _ = ring.run(q, segs, [(k, v)], [segs], 0, True, scale=scale)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wid)
+    held = [torch.randn(k.shape, device="cuda", generator=gen) for _ in range(2)]
+    res = {}
+    for sp in (False, True):
+        for acc in (None, [tuple(t.clone() for t in held)]):
+            res[sp, acc is None] = ring.run_bwd(q, segs, [(k, v)], [segs], 0, True, out, lse, do, scale=scale,
+                                                dkv=acc, split=sp)
+    torch.cuda.synchronize()
+    for fresh in (True, False):
+        (dq0, kv0), (dq1, kv1) = res[False, fresh], res[True, fresh]
+        assert torch.equal(dq0, dq1)
+        for a, b in zip(kv0[0], kv1[0]):
+            assert torch.allclose(b, a, rtol=1e-5, atol=1e-5 * a.abs().max().item()), f"fresh={fresh}"
+    dq, kv = res[True, True]
+    qc, kc, vc, dc = (seeded.exact_f64(t.cpu()) for t in (q, k, v, do))
+    pos = np.arange(L)
+    for b in range(B):
+        rq, rk, rv = oracle.grouped_attention_grads(qc[b], pos, kc[b], vc[b], pos, scale, True, dc[b])
+        grad_close(dq[b].cpu().double().numpy(), rq, f"split dq b{b}")
+        grad_close(kv[0][0][b].cpu().double().numpy(), rk, f"split dk b{b}")
+        grad_close(kv[0][1][b].cpu().double().numpy(), rv, f"split dv b{b}")
+        # with accumulators that held other sums, those sums plus the same gradients
+        _, kva = res[True, False]
+        grad_close(kva[0][0][b].cpu().double().numpy() - held[0][b].cpu().double().numpy(), rk, f"split dk+held b{b}")
+        grad_close(kva[0][1][b].cpu().double().numpy() - held[1][b].cpu().double().numpy(), rv, f"split dv+held b{b}")
+
+
+def test_bwd_split_at_the_32k_share(gpu_lib):
+    # the opt-in split diagonal step at the grouped 32K share (32 query heads
+    # over 8 K/V heads, rank 0), with and without the second dK/dV stream:
+    # dq is bitwise the unsplit one and dk, dv agree with it up to the order
+    # of the fp32 sums (only the diagonal block's accumulators differ at all)
+    w = configs.LLM_32K_CP4_GQA
+    banner(f"backward ring, {w.name} rank 0: split diagonal step against the unsplit one")
+    case = RingCase(w, 0)
+    out, lse, _ = ring.run(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, scale=w.scale)
+    do = seeded.gen_bhsd_at(w.wid, DOUT, w.B, w.H, ringcase_positions(w, 0), w.d, w.dtype, "cuda")
+    ref = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, out, lse, do, scale=w.scale)
+    for ov in (True, False):
+        dq, dkv = ring.run_bwd(case.q, case.q_segs, case.kv, case.kv_segs, 0, True, out, lse, do, scale=w.scale,
+                               split=True, overlap=ov)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, ref[0])
+        for t, ((a, b), (c, e)) in enumerate(zip(ref[1], dkv)):
+            for x, y in ((a, c), (b, e)):
+                if t != 0:
+                    assert torch.equal(x, y), f"block {t}"
+                else:
+                    assert torch.allclose(y, x, rtol=1e-5, atol=1e-5 * x.abs().max().item()), f"overlap={ov}"
+
+
 # ---- the alternatives to the ring: all-gather and all-to-all on heads ------------------
 
 from context_attention_ra_amd import variants  # noqa: E402
