@@ -54,6 +54,7 @@ constexpr int kQAhead = 3;            // LDS operands read ahead of their MFMA (
 constexpr int kKW = 8;                // waves per workgroup of the dK/dV kernel
 constexpr int kKThreads = 64 * kKW;
 constexpr int kKOwn = 32 * kKW;       // owned keys per workgroup of the dK/dV kernel
+constexpr int kKAhead = 4;            // LDS operands read ahead of their MFMA (dK/dV kernel)
 using namespace tiles;
 static_assert(BLay<128>::NRUN % kKW == 0 && BLay<64>::NRUN % kKW == 0 && kQW == kKW,
               "load runs must split evenly over the waves");
@@ -317,11 +318,14 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // dK, dV: owned keys, streamed Q/dO tiles. Eight waves (256 owned keys): the
 // owned V rows sit in LDS (four 64-row tiles of the same layout) and are read
-// as B operands (half of their k-steps from registers), which keeps a wave
-// within 256 registers, so two waves share each SIMD. (The dQ kernel's ping-pong does not pay here: the scores of a
-// whole next tile do not fit beside the two accumulators, and with half-tile
-// units each matrix phase reads about as many LDS bytes per product as the
-// LDS delivers.)
+// as B operands, which keeps a wave within 256 registers, so two waves share
+// each SIMD. Every LDS operand of a tile is read kKAhead products before the
+// product that uses it (one stream per tile through a ring of registers, its
+// order held by scheduling barriers): the compiler by itself keeps one or two
+// reads in flight and waits on the LDS before almost every product. (The dQ
+// kernel's ping-pong does not pay here: the scores of a whole next tile do not
+// fit beside the two accumulators, and with half-tile units each matrix phase
+// reads about as many LDS bytes per product as the LDS delivers.)
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -424,13 +428,12 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   store_rowv(0);
   __syncthreads();
-  // the first half of the k-steps of this wave's owned V rows stay in
-  // registers (as many as fit beside the accumulators), which spares the
-  // LDS a quarter of its row reads
-  constexpr int NVR = KS / 2;
-  bf16x8 vf[NVR];
-#pragma unroll
-  for (int s = 0; s < NVR; ++s) vf[s] = row_operand<D>(vw, w & 1, s, l32, h);
+  // the LDS operand stream of a tile, each read AH products ahead: for each
+  // 32-row half st, the S and dP products' operands (per k-step: Q rows, dO
+  // rows, this wave's owned V rows), then the accumulation products'
+  // (transposing reads of dO and Q)
+  constexpr int AH = kKAhead;
+  constexpr int NE1 = 3 * KS, NE2 = 4 * DT, NEH = NE1 + NE2, NE = 2 * NEH;
   for (int32_t n = 0; n < ntiles; ++n) {
     if (n + 1 < ntiles) {
       fetch_rowv(n + 1);
@@ -448,15 +451,36 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
       (void)qhi;
       need_mask = w_khi > qlo;
     }
+    auto entry = [&](int e) RA_BINLINE -> bf16x8 {
+      const int st = e / NEH, j = e % NEH;
+      if (j < NE1) {
+        const int ksi = j / 3, which = j % 3;
+        if (which == 0) return row_operand<D>(qt, st, ksi, l32, h);
+        if (which == 1) return row_operand<D>(dt, st, ksi, l32, h);
+        return row_operand<D>(vw, w & 1, ksi, l32, h);
+      }
+      const int k = j - NE1, t = k / 4, u = k % 4;
+      return tr_operand<D>(u < 2 ? dt : qt, trb, 2 * st + (u & 1), t);
+    };
+    bf16x8 ring[AH];
+#pragma unroll
+    for (int e = 0; e < AH; ++e) ring[e] = entry(e);
+    auto refill = [&](int e) RA_BINLINE {
+      if (e + AH < NE) ring[e % AH] = entry(e + AH);
+    };
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       f32x16 s = f32x16{}, dpv = f32x16{};
 #pragma unroll
       for (int ksi = 0; ksi < KS; ++ksi) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qt, st, ksi, l32, h), kf[ksi], s, 0, 0, 0);
-        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            row_operand<D>(dt, st, ksi, l32, h), ksi < NVR ? vf[ksi] : row_operand<D>(vw, w & 1, ksi, l32, h),
-            dpv, 0, 0, 0);
+        const int e = st * NEH + 3 * ksi;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[e % AH], kf[ksi], s, 0, 0, 0);
+        refill(e);
+        __builtin_amdgcn_sched_barrier(0);
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[(e + 1) % AH], ring[(e + 2) % AH], dpv, 0, 0, 0);
+        refill(e + 1);
+        refill(e + 2);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // masked scores become -inf (weight exactly 0) in one block, so that
       // the exponentials below are straight-line code
@@ -483,15 +507,19 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
           ds[r] = pv * (dpv[r] - d4[j]);
         }
       }
-      bf16x8 p0, p1, s0, s1;
-      pack_b(p, p0, p1);
-      pack_b(ds, s0, s1);
+      bf16x8 pk[4];
+      pack_b(p, pk[0], pk[1]);
+      pack_b(ds, pk[2], pk[3]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        av[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dt, trb, 2 * st, t), p0, av[t], 0, 0, 0);
-        av[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dt, trb, 2 * st + 1, t), p1, av[t], 0, 0, 0);
-        ak[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qt, trb, 2 * st, t), s0, ak[t], 0, 0, 0);
-        ak[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qt, trb, 2 * st + 1, t), s1, ak[t], 0, 0, 0);
+      for (int k = 0; k < NE2; ++k) {
+        const int e = st * NEH + NE1 + k, t = k / 4, u = k % 4;
+        if (u < 2)
+          av[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[e % AH], pk[u], av[t], 0, 0, 0);
+        else
+          ak[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[e % AH], pk[u], ak[t], 0, 0, 0);
+        refill(e);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);

@@ -6,7 +6,9 @@ progress during the step if one of its waves fits on a SIMD next to the two
 step waves: the d = 128 step kernels must stay within 248 VGPRs (no AGPRs, no
 scratch), and the pass kernel within 16 (512 registers per SIMD lane). The
 kernels are compiled for gfx950 with the library's own flags and the
-footprints read from the compiler's resource report.
+footprints read from the compiler's resource report. The backward kernels
+hold their LDS operands a few products ahead in registers; they must still fit
+two waves per SIMD without spilling.
 """
 
 import os
@@ -68,3 +70,12 @@ def test_pass_kernel_fits_beside_a_step(hipcc_available):
     assert r["ScratchSize [bytes/lane]"] == 0, r
     # two step waves of 248 and one pass wave fill at most the 512 registers of a SIMD lane
     assert 2 * 248 + 16 <= 512
+
+
+def test_backward_kernels_fit_two_waves_per_simd_without_spills(hipcc_available):
+    rep = resource_report("bwd_mfma.hip")
+    kern = {k: v for k, v in rep.items() if "bwd_dq_kernel" in k or "bwd_dkdv_kernel" in k}
+    assert len(kern) == 8, sorted(rep)  # dQ and dK/dV, d = 64 and 128, causal or not
+    for name, r in kern.items():
+        assert r["ScratchSize [bytes/lane]"] == 0, (name, r)
+        assert r["Occupancy [waves/SIMD]"] >= 2, (name, r)
