@@ -459,7 +459,10 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
         if (which == 1) return row_operand<D>(dt, st, ksi, l32, h);
         return row_operand<D>(vw, w & 1, ksi, l32, h);
       }
-      const int k = j - NE1, t = k / 4, u = k % 4;
+      // accumulation product k: operand u (dO slice 2st, 2st+1, Q slice 2st,
+      // 2st+1) of output tile t, t varying fastest, so that the two products
+      // into one accumulator have three others between them
+      const int k = j - NE1, u = k / DT, t = k % DT;
       return tr_operand<D>(u < 2 ? dt : qt, trb, 2 * st + (u & 1), t);
     };
     bf16x8 ring[AH];
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < NE2; ++k) {
-        const int e = st * NEH + NE1 + k, t = k / 4, u = k % 4;
+        const int e = st * NEH + NE1 + k, u = k / DT, t = k % DT;
         if (u < 2)
           av[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[e % AH], pk[u], av[t], 0, 0, 0);
         else
