@@ -136,6 +136,20 @@ def run(q: torch.Tensor,
     return out, lse, state
 
 
+def group_half(x: torch.Tensor, H_kv: int, p: int) -> torch.Tensor:
+    """Half p (0 or 1) of every K/V head's query heads of x [B, H, ...], as a
+    contiguous [B, H/2, ...] tensor. Query head h belongs to K/V head h // G
+    (G = H / H_kv, even); half p holds heads j*G + p*G/2 .. j*G + (p+1)*G/2 - 1
+    of every group j, so that K/V head j of the half serves its heads
+    j*G/2 .. (j+1)*G/2 - 1, the grouping the kernels assume."""
+    B, H = x.shape[:2]
+    G = H // H_kv
+    if G * H_kv != H or G % 2:
+        raise ValueError("group_half needs an even number of query heads per K/V head")
+    g = x.reshape(B, H_kv, G, *x.shape[2:])[:, :, p * (G // 2):(p + 1) * (G // 2)]
+    return g.reshape(B, H // 2, *x.shape[2:]).contiguous()
+
+
 def run_bwd(q: torch.Tensor,
             q_segs: Sequence[Tuple[int, int]],
             kv_blocks: Sequence[Tuple[torch.Tensor, torch.Tensor]],
@@ -218,13 +232,7 @@ def run_bwd(q: torch.Tensor,
     dq = torch.empty((B, H, Lq, d), dtype=torch.float32, device=dev)
     halves = None
     if split and rank in order:
-        # query head h belongs to K/V head h // G; half p holds the query
-        # heads G/2 * p .. G/2 * (p + 1) - 1 of every group, as contiguous
-        # copies, so K/V head j of a half serves its heads j*G/2 .. j*G/2+G/2-1
-        def half(x, p):
-            g = x.view(B, H_kv, G, *x.shape[2:])[:, :, p * (G // 2):(p + 1) * (G // 2)]
-            return g.reshape(B, H // 2, *x.shape[2:]).contiguous()
-        halves = [tuple(half(x, p) for x in (q, dout, lse, delta)) for p in (0, 1)]
+        halves = [tuple(group_half(x, H_kv, p) for x in (q, dout, lse, delta)) for p in (0, 1)]
         # a stand-in of the right shape for the halves' dq argument, which the
         # dK/dV-only launches neither read nor write
         dq_unused = dq.view(-1)[:dq.numel() // 2].view(B, H // 2, Lq, d)

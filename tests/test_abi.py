@@ -320,6 +320,32 @@ def test_backward_split_needs_an_even_group():
         ring.run_bwd(q, [(0, 64)], kv, [[(0, 64)]], 0, True, q, torch.zeros((1, 3, 64)), q, split=True)
 
 
+def test_group_halves_partition_every_group():
+    # the split diagonal step's head halves: together they hold every query
+    # head once, and head i of half p is query head (i // (G/2)) * G +
+    # p * G/2 + i % (G/2), which belongs to K/V head i // (G/2) of the half
+    import torch
+    from context_attention_ra_amd import ring
+    for B, H_kv, G in ((1, 1, 2), (2, 3, 4), (1, 8, 4), (2, 2, 8)):
+        H = H_kv * G
+        x = torch.arange(B * H * 5 * 3, dtype=torch.float32).reshape(B, H, 5, 3)
+        halves = [ring.group_half(x, H_kv, p) for p in (0, 1)]
+        seen = []
+        for p, hx in enumerate(halves):
+            assert hx.shape == (B, H // 2, 5, 3) and hx.is_contiguous()
+            for i in range(H // 2):
+                src = (i // (G // 2)) * G + p * (G // 2) + i % (G // 2)
+                assert src // G == i // (G // 2)  # the same K/V head
+                assert torch.equal(hx[:, i], x[:, src])
+                seen.append(src)
+        assert sorted(seen) == list(range(H))
+        lse = torch.randn(B, H, 5)
+        assert torch.equal(torch.cat([ring.group_half(lse, H_kv, p).reshape(B, H_kv, G // 2, 5)
+                                      for p in (0, 1)], dim=2).reshape(B, H, 5), lse)
+    with pytest.raises(ValueError):
+        ring.group_half(torch.zeros(1, 3, 4), 1, 0)
+
+
 def test_backward_split_refused_under_graph_capture(monkeypatch):
     # the split diagonal step is refused while the current stream captures a
     # graph (checked on the host before any buffer is made or call is made)
